@@ -1,0 +1,121 @@
+"""Seeded synthetic inputs for the gated delta rule core.
+
+This module only draws random tensors: it holds none of the method's arithmetic,
+so both the HIP path and the oracle can be fed from it.  Everything is drawn on
+the host with ``torch.Generator('cpu')`` so a seed always gives the same bits.
+
+Recipe (the workloads of the gated delta rule pages, made synthetic):
+  q, k   ~ N(0, 1) in fp32, then divided by their L2 norm over the key channels
+           (real layers feed unit-length queries and keys into the memory step:
+           "Attention, Part 4", section 6, "Where alpha and beta come from").
+  v      ~ N(0, 1).
+  beta   = sigmoid(N(0, 1))  -- a write strength in (0, 1).
+  log a  ~ U[-0.2, -0.005]  -- the forget gate stored as its logarithm; per key
+           channel for KDA.  alpha = exp(log a) in [0.82, 0.995] brackets the
+           ~94 % per-token retention that "Hybrid attention" (section "A test of
+           memory") reports for a typical head.
+  S0     = std * N(0, 1) in fp32 (zeros when std == 0).
+  Then q, k, v, beta, log a are rounded once to the input dtype (round to nearest
+  even); the oracle is fed exactly those rounded values.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import torch
+
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    B: int
+    H: int
+    T: int
+    Dk: int
+    Dv: int
+    chunk: int
+    dtype: torch.dtype
+    s0_std: float
+    ckpt_every: int = 0
+    kda: bool = False
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    N: int
+    H: int
+    Dk: int
+    Dv: int
+    steps: int
+    dtype: torch.dtype
+    s_std: float
+    kda: bool = False
+
+
+# The five workloads: index = position in the workload list; seed = 1000 + index.
+WORKLOADS = {
+    0: PrefillConfig("gdn_tiny_fp32", 1, 2, 64, 16, 16, 16, torch.float32, 0.0),
+    1: PrefillConfig("gdn_prefill_bf16", 4, 16, 4096, 128, 128, 64, torch.bfloat16, 0.01),
+    2: PrefillConfig("gdn_long_prefill_snapshots_bf16", 1, 32, 65536, 128, 128, 64, torch.bfloat16,
+                     0.01, ckpt_every=8192),
+    3: DecodeConfig("gdn_decode_bf16", 256, 32, 128, 128, 100, torch.bfloat16, 0.02),
+    4: PrefillConfig("kda_prefill_bf16", 2, 32, 8192, 128, 128, 64, torch.bfloat16, 0.01, kda=True),
+}
+
+
+def seed_of(index: int) -> int:
+    return 1000 + index
+
+
+def _unit(x: torch.Tensor) -> torch.Tensor:
+    return x / x.norm(dim=-1, keepdim=True)
+
+
+def make_prefill(B: int, H: int, T: int, Dk: int, Dv: int, dtype: torch.dtype = torch.bfloat16,
+                 *, kda: bool = False, s0_std: float = 0.01, seed: int = 0,
+                 log_alpha_range=(-0.2, -0.005)) -> Dict[str, Optional[torch.Tensor]]:
+    """Draw q, k, v, beta, log_alpha, s0 (in that order) on the host."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = _unit(torch.randn(B, H, T, Dk, generator=g))
+    k = _unit(torch.randn(B, H, T, Dk, generator=g))
+    v = torch.randn(B, H, T, Dv, generator=g)
+    beta = torch.sigmoid(torch.randn(B, H, T, generator=g))
+    lo, hi = log_alpha_range
+    la_shape = (B, H, T, Dk) if kda else (B, H, T)
+    log_alpha = torch.rand(*la_shape, generator=g) * (hi - lo) + lo
+    s0 = (torch.randn(B, H, Dv, Dk, generator=g) * s0_std) if s0_std > 0 else None
+    return {
+        "q": q.to(dtype), "k": k.to(dtype), "v": v.to(dtype),
+        "beta": beta.to(dtype), "log_alpha": log_alpha.to(dtype), "s0": s0,
+    }
+
+
+def make_decode(N: int, H: int, Dk: int, Dv: int, steps: int, dtype: torch.dtype = torch.bfloat16,
+                *, kda: bool = False, s_std: float = 0.02, seed: int = 0,
+                log_alpha_range=(-0.2, -0.005)) -> Dict[str, torch.Tensor]:
+    """Draw the state first, then every step's q, k, v, beta, log_alpha as [steps, ...] tensors."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    state = torch.randn(N, H, Dv, Dk, generator=g) * s_std
+    q = _unit(torch.randn(steps, N, H, Dk, generator=g))
+    k = _unit(torch.randn(steps, N, H, Dk, generator=g))
+    v = torch.randn(steps, N, H, Dv, generator=g)
+    beta = torch.sigmoid(torch.randn(steps, N, H, generator=g))
+    lo, hi = log_alpha_range
+    la_shape = (steps, N, H, Dk) if kda else (steps, N, H)
+    log_alpha = torch.rand(*la_shape, generator=g) * (hi - lo) + lo
+    return {
+        "state": state, "q": q.to(dtype), "k": k.to(dtype), "v": v.to(dtype),
+        "beta": beta.to(dtype), "log_alpha": log_alpha.to(dtype),
+    }
+
+
+def make_workload(index: int):
+    """Inputs of one of the five workloads, with its fixed seed."""
+    c = WORKLOADS[index]
+    if isinstance(c, DecodeConfig):
+        return make_decode(c.N, c.H, c.Dk, c.Dv, c.steps, c.dtype, kda=c.kda, s_std=c.s_std,
+                           seed=seed_of(index))
+    return make_prefill(c.B, c.H, c.T, c.Dk, c.Dv, c.dtype, kda=c.kda, s0_std=c.s0_std,
+                        seed=seed_of(index))
