@@ -1,0 +1,213 @@
+"""MI355X (gfx950) gated delta rule core: Python binding of libgdn.so.
+
+The functions here carry the names of the C ABI in ``include/gdn.h`` and only
+marshal arguments: they check shapes, dtypes and devices, allocate outputs through
+PyTorch when the caller does not pass them, and hand raw device pointers and the
+current HIP stream to the library.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  If ``libgdn.so`` is missing, importing this package
+fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "GdnError", "gdn_chunk_fwd", "kda_chunk_fwd", "gdn_decode_step", "gdn_chunk_workspace_size",
+    "gdn_status_string", "gdn_version", "library_path", "lib",
+    "GDN_F32", "GDN_BF16", "GDN_SUCCESS", "GDN_ERROR_INVALID_VALUE", "GDN_ERROR_NOT_SUPPORTED",
+    "GDN_ERROR_HIP", "GdnChunkDesc",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+GDN_SUCCESS, GDN_ERROR_INVALID_VALUE, GDN_ERROR_NOT_SUPPORTED, GDN_ERROR_HIP = 0, 1, 2, 3
+
+
+class GdnChunkDesc(ctypes.Structure):
+    """Mirror of gdn_chunk_desc_t."""
+    _fields_ = [
+        ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64),
+        ("Dk", ctypes.c_int64), ("Dv", ctypes.c_int64),
+        ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+        ("ckpt_every", ctypes.c_int64),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {gdn_status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(hipcc --offload-arch=gfx950). There is no CPU fallback.")
+    L = ctypes.CDLL(library_path)
+    vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    dp = ctypes.POINTER(GdnChunkDesc)
+    L.gdn_chunk_workspace_size.argtypes = [dp, ci, ctypes.POINTER(sz)]
+    L.gdn_chunk_workspace_size.restype = ci
+    for name in ("gdn_chunk_fwd", "kda_chunk_fwd"):
+        f = getattr(L, name)
+        f.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        f.restype = ci
+    L.gdn_decode_step.argtypes = [i64, i64, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.gdn_decode_step.restype = ci
+    L.gdn_status_string.argtypes = [ci]
+    L.gdn_status_string.restype = ctypes.c_char_p
+    L.gdn_version.argtypes = []
+    L.gdn_version.restype = ci
+    return L
+
+
+lib = _load()
+
+
+def gdn_status_string(status: int) -> str:
+    return lib.gdn_status_string(int(status)).decode()
+
+
+def gdn_version() -> int:
+    return int(lib.gdn_version())
+
+
+_DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+
+
+def _code(dt: torch.dtype) -> int:
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}; use torch.float32 or torch.bfloat16")
+    return _DT[dt]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _desc(B, H, T, D, chunk, in_dt, out_dt, ckpt_every) -> GdnChunkDesc:
+    return GdnChunkDesc(B, H, T, D, D, chunk, _code(in_dt), _code(out_dt), ckpt_every)
+
+
+def gdn_chunk_workspace_size(B: int, H: int, T: int, D: int, *, chunk: int = 64,
+                             in_dtype=torch.bfloat16, out_dtype=None, ckpt_every: int = 0,
+                             kda: bool = False) -> int:
+    d = _desc(B, H, T, D, chunk, in_dtype, out_dtype or in_dtype, ckpt_every)
+    n = ctypes.c_size_t(0)
+    st = lib.gdn_chunk_workspace_size(ctypes.byref(d), int(kda), ctypes.byref(n))
+    if st != GDN_SUCCESS:
+        raise GdnError(st, "gdn_chunk_workspace_size")
+    return int(n.value)
+
+
+def _chunk_fwd(kda: bool, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_dtype, o, s_final,
+               s_ckpt, return_final, stream) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, Dk]")
+    B, H, T, D = q.shape
+    dev, in_dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    out_dt = out_dtype or in_dt
+    _check(k, "k", (B, H, T, D), in_dt, dev)
+    _check(v, "v", (B, H, T, D), in_dt, dev)
+    _check(beta, "beta", (B, H, T), in_dt, dev)
+    _check(log_alpha, "log_alpha", (B, H, T, D) if kda else (B, H, T), in_dt, dev)
+    _check(q, "q", (B, H, T, D), in_dt, dev)
+    if s0 is not None:
+        _check(s0, "s0", (B, H, D, D), torch.float32, dev)
+    if o is None:
+        o = torch.empty(B, H, T, D, dtype=out_dt, device=dev)
+    _check(o, "o", (B, H, T, D), out_dt, dev)
+    if s_final is None and return_final:
+        s_final = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    if s_final is not None:
+        _check(s_final, "s_final", (B, H, D, D), torch.float32, dev)
+    n_ck = T // ckpt_every if ckpt_every > 0 else 0
+    if n_ck > 0:
+        if s_ckpt is None:
+            s_ckpt = torch.empty(B, H, n_ck, D, D, dtype=torch.float32, device=dev)
+        _check(s_ckpt, "s_ckpt", (B, H, n_ck, D, D), torch.float32, dev)
+    else:
+        s_ckpt = None
+    d = _desc(B, H, T, D, chunk, in_dt, out_dt, ckpt_every)
+    fn = lib.kda_chunk_fwd if kda else lib.gdn_chunk_fwd
+    st = fn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(s0),
+            _ptr(o), _ptr(s_final), _ptr(s_ckpt), None, 0, _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GdnError(st, "kda_chunk_fwd" if kda else "gdn_chunk_fwd")
+    return o, s_final, s_ckpt
+
+
+def gdn_chunk_fwd(q, k, v, beta, log_alpha, s0=None, *, chunk: int = 64, ckpt_every: int = 0,
+                  out_dtype=None, o=None, s_final=None, s_ckpt=None, return_final: bool = True,
+                  stream=None):
+    """Chunkwise prefill of the gated delta rule (see gdn_chunk_fwd in include/gdn.h).
+
+    q, k [B,H,T,D]; v [B,H,T,D]; beta, log_alpha [B,H,T] (fp32 or bf16, one dtype);
+    s0 [B,H,D,D] fp32 or None.  Returns (o [B,H,T,D], s_final [B,H,D,D] fp32 or None,
+    s_ckpt [B,H,T//ckpt_every,D,D] fp32 or None).  Pass s_final=s0 to update in place.
+    Asynchronous on `stream` (default: torch's current stream).
+    """
+    return _chunk_fwd(False, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_dtype, o,
+                      s_final, s_ckpt, return_final, stream)
+
+
+def kda_chunk_fwd(q, k, v, beta, log_alpha, s0=None, *, chunk: int = 64, ckpt_every: int = 0,
+                  out_dtype=None, o=None, s_final=None, s_ckpt=None, return_final: bool = True,
+                  stream=None):
+    """Chunkwise prefill of KDA: as gdn_chunk_fwd with log_alpha [B,H,T,D] (one rate per key channel)."""
+    return _chunk_fwd(True, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_dtype, o,
+                      s_final, s_ckpt, return_final, stream)
+
+
+def gdn_decode_step(state, q, k, v, beta, log_alpha, *, o=None, out_dtype=None, stream=None):
+    """One decode step on every (sequence, head) fp32 state, in place (gdn_decode_step).
+
+    state [N,H,D,D] fp32 (updated); q, k, v [N,H,D]; beta, log_alpha [N,H].  Returns o [N,H,D].
+    """
+    N, H, D, D2 = state.shape
+    dev, in_dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    _check(state, "state", (N, H, D, D2), torch.float32, dev)
+    for name, t, shp in (("q", q, (N, H, D2)), ("k", k, (N, H, D2)), ("v", v, (N, H, D)),
+                         ("beta", beta, (N, H)), ("log_alpha", log_alpha, (N, H))):
+        _check(t, name, shp, in_dt, dev)
+    out_dt = out_dtype or in_dt
+    if o is None:
+        o = torch.empty(N, H, D, dtype=out_dt, device=dev)
+    _check(o, "o", (N, H, D), out_dt, dev)
+    st = lib.gdn_decode_step(N, H, D2, D, _code(in_dt), _code(out_dt), _ptr(state), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(o), _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GdnError(st, "gdn_decode_step")
+    return o

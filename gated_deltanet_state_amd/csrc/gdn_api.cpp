@@ -1,0 +1,177 @@
+// gdn_api.cpp -- the extern "C" entry points of libgdn.so: synchronous host-side
+// validation, then dispatch to one kernel launch on the caller's stream.
+//
+// Nothing here touches device memory or synchronises; every check runs before the
+// first HIP call, so a rejected call has launched nothing.
+#include <stdint.h>
+#include <string.h>
+
+#include "gdn_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool aligned_elem(const void* p, gdn_dtype_t dt) {
+  const uintptr_t m = dt == GDN_F32 ? 3u : 1u;
+  return (reinterpret_cast<uintptr_t>(p) & m) == 0;
+}
+
+bool valid_dtype(gdn_dtype_t d) { return d == GDN_F32 || d == GDN_BF16; }
+
+// Byte ranges [a, a + na) and [b, b + nb) intersect.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+// Product of non-negative sizes with an overflow guard against 2^62.
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > (INT64_C(1) << 62) / a) return false;
+  *out = a * b;
+  return true;
+}
+
+gdn_status_t check_chunk_desc(const gdn_chunk_desc_t* d, int is_kda, gdn::ChunkArgs* out) {
+  if (!d) return GDN_ERROR_INVALID_VALUE;
+  if (d->B < 0 || d->H < 0 || d->T < 0 || d->Dk <= 0 || d->Dv <= 0) return GDN_ERROR_INVALID_VALUE;
+  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return GDN_ERROR_INVALID_VALUE;
+  if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return GDN_ERROR_INVALID_VALUE;
+  if (d->ckpt_every < 0 || (d->ckpt_every > 0 && d->ckpt_every % d->chunk != 0))
+    return GDN_ERROR_INVALID_VALUE;
+  int64_t tmp;
+  if (!mul_ok(d->B, d->H, &tmp) || !mul_ok(tmp, d->T, &tmp) || !mul_ok(tmp, d->Dk + d->Dv, &tmp))
+    return GDN_ERROR_INVALID_VALUE;
+  if (d->Dk != d->Dv) return GDN_ERROR_NOT_SUPPORTED;
+  gdn::ChunkArgs a;
+  memset(&a, 0, sizeof a);
+  a.B = d->B; a.H = d->H; a.T = d->T; a.D = d->Dk; a.chunk = d->chunk;
+  a.in_dtype = d->in_dtype; a.out_dtype = d->out_dtype; a.ckpt_every = d->ckpt_every;
+  a.n_ckpt = d->ckpt_every > 0 ? d->T / d->ckpt_every : 0;
+  (void)is_kda;
+  if (!gdn::chunk_mfma_supported(a) && !gdn::chunk_valu_supported(a)) return GDN_ERROR_NOT_SUPPORTED;
+  *out = a;
+  return GDN_SUCCESS;
+}
+
+gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, const void* k,
+                       const void* v, const void* beta, const void* log_alpha, const float* s0,
+                       void* o, float* s_final, float* s_ckpt, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  gdn::ChunkArgs a;
+  gdn_status_t st = check_chunk_desc(d, is_kda, &a);
+  if (st != GDN_SUCCESS) return st;
+  (void)workspace;
+  (void)workspace_bytes;  // the fused kernels need no workspace (size 0)
+  const int64_t BH = a.B * a.H;
+  if (BH == 0) return GDN_SUCCESS;
+  const size_t state_bytes = (size_t)BH * (size_t)(a.D * a.D) * sizeof(float);
+  const size_t in_elem = a.in_dtype == GDN_F32 ? 4 : 2;
+  const size_t out_elem = a.out_dtype == GDN_F32 ? 4 : 2;
+  const size_t o_bytes = (size_t)BH * (size_t)a.T * (size_t)a.D * out_elem;
+  if (a.T > 0) {
+    if (!q || !k || !v || !beta || !log_alpha || !o) return GDN_ERROR_INVALID_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GDN_ERROR_INVALID_VALUE;
+    if (!aligned_elem(beta, a.in_dtype) || !aligned_elem(log_alpha, a.in_dtype))
+      return GDN_ERROR_INVALID_VALUE;
+    if (is_kda && !aligned16(log_alpha)) return GDN_ERROR_INVALID_VALUE;
+  }
+  if (s0 && !aligned16(s0)) return GDN_ERROR_INVALID_VALUE;
+  if (s_final && !aligned16(s_final)) return GDN_ERROR_INVALID_VALUE;
+  if (a.n_ckpt > 0) {
+    if (!s_ckpt || !aligned16(s_ckpt)) return GDN_ERROR_INVALID_VALUE;
+  } else {
+    s_ckpt = nullptr;
+  }
+  // s_final may be s0 exactly (in place); any other overlap among the state buffers or
+  // with o is rejected.
+  if (s0 && s_final && (const void*)s0 != (const void*)s_final &&
+      overlaps(s0, state_bytes, s_final, state_bytes))
+    return GDN_ERROR_INVALID_VALUE;
+  const size_t ck_bytes = (size_t)a.n_ckpt * state_bytes;
+  if (s_ckpt && (overlaps(s_ckpt, ck_bytes, s0, s0 ? state_bytes : 0) ||
+                 overlaps(s_ckpt, ck_bytes, s_final, s_final ? state_bytes : 0) ||
+                 overlaps(s_ckpt, ck_bytes, o, o_bytes)))
+    return GDN_ERROR_INVALID_VALUE;
+  if (o && (overlaps(o, o_bytes, s0, s0 ? state_bytes : 0) ||
+            overlaps(o, o_bytes, s_final, s_final ? state_bytes : 0)))
+    return GDN_ERROR_INVALID_VALUE;
+  (void)in_elem;
+
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
+  a.s0 = s0; a.o = o; a.s_final = s_final; a.s_ckpt = s_ckpt;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = gdn::chunk_mfma_supported(a) ? gdn::launch_chunk_mfma(a, is_kda != 0, s)
+                          : gdn::launch_chunk_valu(a, is_kda != 0, s);
+  return e == hipSuccess ? GDN_SUCCESS : GDN_ERROR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status_t gdn_chunk_workspace_size(const gdn_chunk_desc_t* d, int is_kda, size_t* bytes) {
+  if (!bytes) return GDN_ERROR_INVALID_VALUE;
+  gdn::ChunkArgs a;
+  gdn_status_t st = check_chunk_desc(d, is_kda, &a);
+  if (st != GDN_SUCCESS) return st;
+  *bytes = 0;
+  return GDN_SUCCESS;
+}
+
+gdn_status_t gdn_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                           const void* beta, const void* log_alpha, const float* s0, void* o,
+                           float* s_final, float* s_ckpt, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return chunk_fwd(0, d, q, k, v, beta, log_alpha, s0, o, s_final, s_ckpt, workspace,
+                   workspace_bytes, stream);
+}
+
+gdn_status_t kda_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                           const void* beta, const void* log_alpha, const float* s0, void* o,
+                           float* s_final, float* s_ckpt, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return chunk_fwd(1, d, q, k, v, beta, log_alpha, s0, o, s_final, s_ckpt, workspace,
+                   workspace_bytes, stream);
+}
+
+gdn_status_t gdn_decode_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv, gdn_dtype_t in_dtype,
+                             gdn_dtype_t out_dtype, float* state, const void* q, const void* k,
+                             const void* v, const void* beta, const void* log_alpha, void* o,
+                             void* stream) {
+  if (N < 0 || H < 0 || Dk <= 0 || Dv <= 0) return GDN_ERROR_INVALID_VALUE;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GDN_ERROR_INVALID_VALUE;
+  int64_t tmp;
+  if (!mul_ok(N, H, &tmp) || !mul_ok(tmp, Dk * Dv, &tmp)) return GDN_ERROR_INVALID_VALUE;
+  if (Dk != Dv) return GDN_ERROR_NOT_SUPPORTED;
+  gdn::DecodeArgs a;
+  a.N = N; a.H = H; a.D = Dk; a.in_dtype = in_dtype; a.out_dtype = out_dtype;
+  if (!gdn::decode_supported(a)) return GDN_ERROR_NOT_SUPPORTED;
+  if (N * H == 0) return GDN_SUCCESS;
+  if (!state || !q || !k || !v || !beta || !log_alpha || !o) return GDN_ERROR_INVALID_VALUE;
+  if (!aligned16(state) || !aligned_elem(q, in_dtype) || !aligned_elem(k, in_dtype) ||
+      !aligned_elem(v, in_dtype) || !aligned_elem(beta, in_dtype) ||
+      !aligned_elem(log_alpha, in_dtype) || !aligned_elem(o, out_dtype))
+    return GDN_ERROR_INVALID_VALUE;
+  const size_t state_bytes = (size_t)(N * H) * (size_t)(Dk * Dv) * sizeof(float);
+  const size_t o_bytes = (size_t)(N * H) * (size_t)Dv * (out_dtype == GDN_F32 ? 4 : 2);
+  if (overlaps(state, state_bytes, o, o_bytes)) return GDN_ERROR_INVALID_VALUE;
+  a.state = state; a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha; a.o = o;
+  hipError_t e = gdn::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_SUCCESS : GDN_ERROR_HIP;
+}
+
+const char* gdn_status_string(gdn_status_t s) {
+  switch (s) {
+    case GDN_SUCCESS: return "success";
+    case GDN_ERROR_INVALID_VALUE: return "invalid value (null/misaligned pointer, bad size or option, overlapping buffers)";
+    case GDN_ERROR_NOT_SUPPORTED: return "combination of head size, chunk and dtypes not supported";
+    case GDN_ERROR_HIP: return "HIP runtime error or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+int gdn_version(void) { return GDN_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// gdn_internal.h -- launch descriptors shared by the host API and the HIP kernels of
+// libgdn.so.  Not part of the public ABI (include/gdn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+// One chunkwise prefill call after host-side validation.
+struct ChunkArgs {
+  int64_t B, H, T, D;      // Dk == Dv == D
+  int chunk;
+  gdn_dtype_t in_dtype, out_dtype;
+  int64_t ckpt_every;      // 0 = none
+  int64_t n_ckpt;          // snapshots per stream = T / ckpt_every (0 when disabled)
+  const void *q, *k, *v, *beta, *log_alpha;
+  const float* s0;         // may be null
+  void* o;
+  float* s_final;          // may be null
+  float* s_ckpt;           // may be null iff n_ckpt == 0
+};
+
+struct DecodeArgs {
+  int64_t N, H, D;
+  gdn_dtype_t in_dtype, out_dtype;
+  float* state;
+  const void *q, *k, *v, *beta, *log_alpha;
+  void* o;
+};
+
+// Matrix-core prefill (bf16 inputs, D = 128, chunk = 64).
+bool chunk_mfma_supported(const ChunkArgs& a);
+hipError_t launch_chunk_mfma(const ChunkArgs& a, bool kda, hipStream_t stream);
+
+// fp32 vector-unit prefill (fp32 or bf16 inputs, D in {16,32,64,128}, chunk in {16,32,64}).
+bool chunk_valu_supported(const ChunkArgs& a);
+hipError_t launch_chunk_valu(const ChunkArgs& a, bool kda, hipStream_t stream);
+
+// Decode step (D in {16,32,64,128}).
+bool decode_supported(const DecodeArgs& a);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,156 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule library (libgdn.so).
+ *
+ * The library computes the gated delta rule
+ *
+ *     S_t = alpha_t * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t
+ *
+ * ("Hybrid models: what Gated DeltaNet replaces in the KV cache", section "Gated
+ * DeltaNet: add decay"; the query reads the updated state, "From Traditional Attention
+ * to hybrid ones", section 5) and its per-channel-decay variant KDA
+ *
+ *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *
+ * ("From Traditional Attention to hybrid ones", section 7).  The state S is d_v x d_k
+ * (row = value channel, column = key channel), kept in fp32.  The gate is passed as
+ * log_alpha = g (g = log alpha, "Attention, Part 4", "Where alpha and beta come from").
+ *
+ * Conventions shared by every entry point
+ *  - Tensor pointers are DEVICE pointers to contiguous row-major arrays with the
+ *    layouts given below; q, k, v, o, s0, s_final, s_ckpt and state must be 16-byte
+ *    aligned.  `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - The caller owns every buffer.  The library allocates nothing, frees nothing and
+ *    keeps no pointer after a call returns.  Outputs are overwritten entirely.
+ *  - Arguments are validated synchronously on the host before anything is launched;
+ *    on any error nothing is launched and the status says why.  Work is enqueued
+ *    asynchronously on `stream`; the library never synchronises.  A failed launch
+ *    returns GDN_ERROR_HIP.  The library holds no mutable global state, so calls from
+ *    several host threads are safe.
+ *  - Device VALUES are not checked.  Preconditions: log_alpha finite and <= 0
+ *    (alpha in (0, 1]); beta finite (in (0, 1) on the pages); |q|, |k|, |v| <= 65504
+ *    for bf16 inputs (the prefill kernels use half-precision matrix-core operands).
+ *    Queries and keys are expected to be L2-normalised by the caller (the core does
+ *    not normalise and applies no 1/sqrt(d) scale), but this is not required.
+ *    Invalid values give NaN/Inf in the outputs, never a fault.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_VERSION 100 /* 1.0.0 */
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
+
+typedef enum {
+  GDN_SUCCESS = 0,
+  GDN_ERROR_INVALID_VALUE = 1, /* NULL / misaligned pointer, bad size, bad ckpt_every, overlap */
+  GDN_ERROR_NOT_SUPPORTED = 2, /* (Dk, Dv, chunk, dtype) combination not compiled in */
+  GDN_ERROR_HIP = 3            /* a HIP runtime call or kernel launch failed */
+} gdn_status_t;
+
+/* Shape and options of one chunkwise prefill call. */
+typedef struct {
+  int64_t B, H, T;      /* batch, heads, tokens; T >= 0 (T = 0: no outputs but s_final = s0) */
+  int64_t Dk, Dv;       /* key / value head dimensions */
+  int32_t chunk;        /* tokens per chunk: 16, 32 or 64.  The result does not depend on it
+                           beyond rounding: the chunked form is exact ("Hybrid attention",
+                           section "Training a recurrence in parallel").  A ragged tail
+                           (T % chunk != 0) is handled as if padded with identity steps
+                           (beta = 0, log_alpha = 0: "Attention, Part 4", section 6). */
+  gdn_dtype_t in_dtype; /* dtype of q, k, v, beta, log_alpha (all the same) */
+  gdn_dtype_t out_dtype;/* dtype of o */
+  int64_t ckpt_every;   /* 0 = no snapshots; else a positive multiple of `chunk` */
+} gdn_chunk_desc_t;
+
+/*
+ * Bytes of device workspace that gdn_chunk_fwd / kda_chunk_fwd need for `d`
+ * (is_kda = 0 or 1).  The fused prefill kernels need none: *bytes is set to 0 for
+ * every supported combination.  Errors as for gdn_chunk_fwd's validation.
+ */
+gdn_status_t gdn_chunk_workspace_size(const gdn_chunk_desc_t* d, int is_kda, size_t* bytes);
+
+/*
+ * Chunkwise-parallel prefill of the gated delta rule with initial state, final state
+ * and chunk-boundary snapshots.
+ *
+ * Method: the sequence is cut into chunks of `chunk` tokens; inside a chunk the updates
+ * are dense matrix products and a small unit lower-triangular system, and only the
+ * state is handed from one chunk to the next ("Hybrid Linear Attention Architecture
+ * Design Explained", section 4, cross-chunk state update and intra-chunk output;
+ * "Hybrid attention", section "Training a recurrence in parallel"; "Hybrid models...",
+ * section "What a recurrent state changes for serving", prefill takes a chunked path).
+ * Snapshot n (0-based) is the state after token (n+1)*ckpt_every: the state at a
+ * position N cannot be recovered from a later one, so prefix reuse needs a snapshot
+ * taken at N ("Hybrid models...", same section, item 1).  Resuming from a snapshot is
+ * passing it as s0.
+ *
+ * Arguments (device pointers):
+ *   q, k      [B, H, T, Dk]   in_dtype
+ *   v         [B, H, T, Dv]   in_dtype
+ *   beta      [B, H, T]       in_dtype
+ *   log_alpha [B, H, T]       in_dtype
+ *   s0        [B, H, Dv, Dk]  fp32, or NULL for a zero initial state
+ *   o         [B, H, T, Dv]   out_dtype, written
+ *   s_final   [B, H, Dv, Dk]  fp32, written, or NULL.  May be exactly s0 (updated in
+ *                             place); any other overlap with s0 is INVALID_VALUE.
+ *   s_ckpt    [B, H, T / ckpt_every, Dv, Dk] fp32, written; required (non-NULL) when
+ *                             ckpt_every > 0 and T >= ckpt_every, ignored otherwise.
+ *   workspace, workspace_bytes: at least gdn_chunk_workspace_size() bytes (NULL / 0 ok
+ *                             when that is 0).
+ * Supported: Dk == Dv; bf16 inputs with Dk = 128 and chunk = 64 run on the matrix
+ * cores; fp32 or bf16 inputs with Dk in {16, 32, 64, 128} and any allowed chunk run on
+ * the fp32 vector path.  Other combinations: GDN_ERROR_NOT_SUPPORTED.
+ */
+gdn_status_t gdn_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                           const void* beta, const void* log_alpha, const float* s0, void* o,
+                           float* s_final, float* s_ckpt, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Chunkwise prefill of KDA (per-channel decay): identical to gdn_chunk_fwd except
+ *   log_alpha [B, H, T, Dk]   in_dtype: one forget rate per key channel
+ * ("Attention, Part 4", section 7; "Hybrid Linear Attention Architecture Design
+ * Explained", sections 3.1 and 4 -- the division form of the intra-chunk products needs
+ * overflow protection, which the kernels provide by per-sub-block reference points).
+ */
+gdn_status_t kda_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                           const void* beta, const void* log_alpha, const float* s0, void* o,
+                           float* s_final, float* s_ckpt, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * One recurrent (decode) step of the gated delta rule for every live sequence: each
+ * sequence keeps a fixed-size state that is updated in place once per token
+ * ("From Traditional Attention to hybrid ones", section "vLLM Storage": the state is
+ * fixed per live sequence and updated in place; "Attention, Part 4", section 8).
+ *
+ *   state     [N, H, Dv, Dk]  fp32, read and overwritten in place
+ *   q, k      [N, H, Dk]      in_dtype
+ *   v         [N, H, Dv]      in_dtype
+ *   beta      [N, H]          in_dtype
+ *   log_alpha [N, H]          in_dtype
+ *   o         [N, H, Dv]      out_dtype, written
+ * N >= 0 (N = 0 or H = 0 is a no-op).  Supported: Dk == Dv in {16, 32, 64, 128}.
+ */
+gdn_status_t gdn_decode_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv, gdn_dtype_t in_dtype,
+                             gdn_dtype_t out_dtype, float* state, const void* q, const void* k,
+                             const void* v, const void* beta, const void* log_alpha, void* o,
+                             void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* gdn_status_string(gdn_status_t s);
+
+/* GDN_VERSION of the built library. */
+int gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */
