@@ -1,0 +1,279 @@
+"""Benchmark of the gated delta rule core on one MI355X.
+
+One JSON line on stdout.  The timed step is one chunkwise prefill of the headline
+workload (B=4 sequences x T=4096 tokens, H=16 heads of d_k = d_v = 128, chunk 64, bf16
+q/k/v/beta/log alpha, fp32 state, bf16 outputs, final state out): `value` is Mtok/s
+(B*T tokens per second, each token carrying all 16 heads), inputs resident in HBM.
+Beside it, with their own timings: the recurrent decode step (256 sequences x 32 heads of
+128x128 fp32 states, 100 in-place steps; state GB/s), the long prefill with snapshots
+(T = 65536, 32 heads, a snapshot every 8192 tokens) and the KDA prefill.
+
+`roofline` is measured live with HIP events on the stream the kernels run on;
+`cpu_baseline` times the fp64 oracle on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN chunkwise prefill Mtok/s at H=16,d=128 (MFMA %); decode state GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
+
+
+def prefill_flops_per_head_token(C: int, d: int) -> int:
+    """Algorithmic flops per head-token of the chunkwise prefill with C x C products counted as
+    full tiles: K K^T, Q K^T (2 C d each), W/U-type products T X and P U (2 C d each, 2 of
+    them at d_v = d), and the three state-coupled d x d products K S^T, Q S^T, U^T K (2 d^2
+    each): 10 C d + 6 d^2."""
+    return 10 * C * d + 6 * d * d
+
+
+def prefill_bytes(B, H, T, d, in_bytes=2, out_bytes=2, n_ckpt=0, kda=False, s0=True) -> int:
+    """Compulsory HBM traffic: q, k, v, beta, log alpha in; o out; S0 in, S_final and the
+    snapshots out (fp32)."""
+    per_tok = (3 * d + 1 + (d if kda else 1)) * in_bytes + d * out_bytes
+    state = d * d * 4
+    return B * H * (T * per_tok + state * ((1 if s0 else 0) + 1 + n_ckpt))
+
+
+def _src_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_deltanet_state_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str, src_files, per_launch_fallback=None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("src_sha256_16") != _src_hash(*src_files):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_launches(fn, steps: int, warmup: int, torch) -> float:
+    """Average ms per call of fn(i) over `steps` calls, HIP events on torch's current stream
+    (the stream every launch goes to)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def cpu_baseline_prefill(inp, n_streams: int, H: int):
+    """fp64 oracle on `n_streams` whole (batch, head) streams of the workload, all host cores."""
+    import oracle
+    oracle.build(force=False)
+    B, Hh, T, d = inp["q"].shape
+    sel = [(i // Hh, i % Hh) for i in range(n_streams)]
+    sub = {k: (inp[k][[b for b, _ in sel], [h for _, h in sel]].unsqueeze(0).contiguous()
+               if inp[k] is not None else None) for k in inp}
+    t0 = time.perf_counter()
+    _, _, _, threads = oracle.forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["log_alpha"], sub["s0"],
+                                      return_threads=True)
+    dt = time.perf_counter() - t0
+    tokens = n_streams * T / H  # a token carries all H heads
+    return {"value": round(tokens / dt / 1e6, 6), "unit": "Mtok/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_streams} of {B * Hh} (batch, head) streams, all {T} tokens each, fp64 token loop; "
+                      f"{dt:.2f} s wall; throughput scaled to tokens of {H} heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "kda", "all"], default="all",
+                    help="run a subset (for profiling); the JSON line needs 'all' or 'prefill'")
+    ap.add_argument("--cpu-streams", type=int, default=0, help="oracle sample size (0 = host cores)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the (batch, head) streams shard with no exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_state_amd as g
+    from gated_deltanet_state_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    out = {}
+    extra = {}
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    # ---------------- headline: chunkwise prefill, B=4 H=16 T=4096 d=128 C=64 ----------------
+    if args.only in ("prefill", "all"):
+        c = synth.WORKLOADS[1]
+        log("prefill: generating inputs")
+        sets = [synth.make_workload(1), synth.make_prefill(c.B, c.H, c.T, c.Dk, c.Dv, c.dtype,
+                                                             s0_std=c.s0_std, seed=synth.seed_of(1) + 100)]
+        dsets = [{k: v.to(dev) for k, v in s.items()} for s in sets]
+        outs = [(torch.empty(c.B, c.H, c.T, c.Dv, dtype=torch.bfloat16, device=dev),
+                 torch.empty(c.B, c.H, c.Dv, c.Dk, dtype=torch.float32, device=dev)) for _ in dsets]
+
+        def step(i):
+            d = dsets[i % 2]
+            o, sf = outs[i % 2]
+            g.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["s0"], chunk=c.chunk,
+                            o=o, s_final=sf)
+
+        log("prefill: timing")
+        ms = time_launches(step, args.steps, args.warmup, torch)
+        tokens = c.B * c.T
+        mtoks = tokens / (ms * 1e-3) / 1e6
+        flops = c.B * c.H * c.T * prefill_flops_per_head_token(c.chunk, c.Dk)
+        nbytes = prefill_bytes(c.B, c.H, c.T, c.Dk)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        tflops = flops / (ms * 1e-3) / 1e12
+        traffic = _traffic("gdn_chunk_mfma", ["gdn_chunk_mfma.hip"])
+        out.update({
+            "metric": METRIC, "value": round(mtoks, 3), "unit": "Mtok/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": c.name, "B": c.B, "H": c.H, "T": c.T, "d_k": c.Dk, "d_v": c.Dv,
+                       "chunk": c.chunk, "inputs": "bf16", "state": "fp32", "o": "bf16",
+                       "global_batch": c.B, "seq_len": c.T, "parallelism": "single GPU"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                         "kernel": "gdn_chunk_mfma_kernel", "algorithmic_bytes": nbytes},
+            "mfma": {"achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops},
+        })
+        log(f"prefill: {ms*1e3:.1f} us/step, {mtoks:.1f} Mtok/s, {gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
+        if not args.no_cpu_baseline:
+            import oracle
+            oracle.build(force=False)
+            n = args.cpu_streams or min(c.B * c.H, oracle.hardware_threads())
+            log(f"cpu baseline: oracle on {n} streams")
+            out["cpu_baseline"] = cpu_baseline_prefill(sets[0], n, c.H)
+        del dsets, outs, sets
+        torch.cuda.empty_cache()
+
+    # ---------------- decode: 256 x 32 states of 128 x 128 fp32, 100 steps ----------------
+    if args.only in ("decode", "all"):
+        c = synth.WORKLOADS[3]
+        log("decode: generating inputs")
+        inp = synth.make_workload(3)
+        st = inp["state"].to(dev)
+        dq = {k: inp[k].to(dev) for k in ("q", "k", "v", "beta", "log_alpha")}
+        o = torch.empty(c.N, c.H, c.Dv, dtype=torch.bfloat16, device=dev)
+
+        def dstep(i):
+            t = i % c.steps
+            g.gdn_decode_step(st, dq["q"][t], dq["k"][t], dq["v"][t], dq["beta"][t], dq["log_alpha"][t], o=o)
+
+        for i in range(3):
+            dstep(i)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(c.steps):
+            dstep(i)
+        e.record()
+        torch.cuda.synchronize()
+        ms100 = s.elapsed_time(e)
+        per = ms100 / c.steps
+        state_bytes = 2 * c.N * c.H * c.Dk * c.Dv * 4
+        io_bytes = c.N * c.H * ((3 * c.Dk + 2) * 2 + c.Dv * 2)
+        gbs = state_bytes / (per * 1e-3) / 1e9
+        hbm = (state_bytes + io_bytes) / (per * 1e-3) / 1e9
+        extra["decode"] = {
+            "workload": c.name, "N": c.N, "H": c.H, "d": c.Dk, "steps": c.steps,
+            "ms_total": round(ms100, 4), "us_per_step": round(per * 1e3, 3),
+            "state_GBps": round(gbs, 1),
+            "roofline": {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(hbm / HBM_PEAK_GBS, 4),
+                         "traffic": _traffic("gdn_decode", ["gdn_decode.hip"]),
+                         "kernel": "decode_kernel", "algorithmic_bytes": state_bytes + io_bytes},
+        }
+        log(f"decode: {per*1e3:.1f} us/step, state {gbs:.0f} GB/s, HBM frac {hbm/HBM_PEAK_GBS:.3f}")
+        del st, dq, inp
+        torch.cuda.empty_cache()
+
+    # ---------------- long prefill with snapshots: H=32, T=65536 ----------------
+    if args.only in ("long", "all"):
+        c = synth.WORKLOADS[2]
+        log("long prefill: generating inputs")
+        inp = synth.make_workload(2)
+        d = {k: v.to(dev) for k, v in inp.items()}
+        del inp
+        o = torch.empty(c.B, c.H, c.T, c.Dv, dtype=torch.bfloat16, device=dev)
+        sf = torch.empty(c.B, c.H, c.Dv, c.Dk, dtype=torch.float32, device=dev)
+        sc = torch.empty(c.B, c.H, c.T // c.ckpt_every, c.Dv, c.Dk, dtype=torch.float32, device=dev)
+
+        def lstep(i):
+            g.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["s0"], chunk=c.chunk,
+                            ckpt_every=c.ckpt_every, o=o, s_final=sf, s_ckpt=sc)
+
+        ms = time_launches(lstep, 3, 1, torch)
+        nb = prefill_bytes(c.B, c.H, c.T, c.Dk, n_ckpt=c.T // c.ckpt_every)
+        fl = c.B * c.H * c.T * prefill_flops_per_head_token(c.chunk, c.Dk)
+        extra["long_prefill"] = {
+            "workload": c.name, "B": c.B, "H": c.H, "T": c.T, "ckpt_every": c.ckpt_every,
+            "ms": round(ms, 4), "Mtok_per_s": round(c.B * c.T / (ms * 1e-3) / 1e6, 3),
+            "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        log(f"long prefill: {ms:.3f} ms")
+        del d, o, sf, sc
+        torch.cuda.empty_cache()
+
+    # ---------------- KDA prefill: B=2 H=32 T=8192 ----------------
+    if args.only in ("kda", "all"):
+        c = synth.WORKLOADS[4]
+        log("kda: generating inputs")
+        inp = synth.make_workload(4)
+        d = {k: v.to(dev) for k, v in inp.items()}
+        del inp
+        o = torch.empty(c.B, c.H, c.T, c.Dv, dtype=torch.bfloat16, device=dev)
+        sf = torch.empty(c.B, c.H, c.Dv, c.Dk, dtype=torch.float32, device=dev)
+
+        def kstep(i):
+            g.kda_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["s0"], chunk=c.chunk,
+                            o=o, s_final=sf)
+
+        ms = time_launches(kstep, 3, 1, torch)
+        nb = prefill_bytes(c.B, c.H, c.T, c.Dk, kda=True)
+        fl = c.B * c.H * c.T * prefill_flops_per_head_token(c.chunk, c.Dk)
+        extra["kda_prefill"] = {
+            "workload": c.name, "B": c.B, "H": c.H, "T": c.T, "ms": round(ms, 4),
+            "Mtok_per_s": round(c.B * c.T / (ms * 1e-3) / 1e6, 3),
+            "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        log(f"kda prefill: {ms:.3f} ms")
+
+    if "metric" not in out:
+        print(json.dumps(extra))
+        return
+    out.update(extra)
+    out["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

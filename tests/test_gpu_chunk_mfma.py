@@ -1,0 +1,137 @@
+"""Matrix-core chunkwise prefill (bf16 inputs, d = 128, chunk 64) vs the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_deltanet_state_amd import synth
+from helpers import TOL_BF16, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    oracle.build(force=False)
+
+
+def _gpu(kda, inp, ckpt_every=0, out_dtype=None, **kw):
+    import gated_deltanet_state_amd as g
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    fn = g.kda_chunk_fwd if kda else g.gdn_chunk_fwd
+    r = fn(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["s0"], chunk=64, ckpt_every=ckpt_every,
+           out_dtype=out_dtype, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def _ref(kda, inp, ckpt_every=0):
+    return oracle.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], inp["s0"], kda=kda,
+                          ckpt_every=ckpt_every)
+
+
+@pytest.mark.parametrize("T", [1, 64, 200, 1000])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_gdn_mfma_small(T, out_dtype):
+    say(f"mfma gdn T={T} out={out_dtype}")
+    inp = synth.make_prefill(1, 3, T, 128, 128, torch.bfloat16, s0_std=0.01, seed=T)
+    o, sf, _ = _gpu(False, inp, out_dtype=out_dtype)
+    o_ref, s_ref, _ = _ref(False, inp)
+    eo, es = rel_l2(o, o_ref), rel_l2(sf, s_ref)
+    print(f"rel-L2 o={eo:.3e} s_final={es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    if out_dtype == torch.float32:
+        assert eo <= 1e-3  # compute error alone (fp16 operands, fp32 accumulation)
+
+
+def test_gdn_mfma_zero_initial_state_and_empty():
+    import gated_deltanet_state_amd as g
+    say("mfma gdn s0=None, T=0")
+    inp = synth.make_prefill(2, 2, 130, 128, 128, torch.bfloat16, s0_std=0.0, seed=3)
+    o, sf, _ = _gpu(False, inp)
+    o_ref, s_ref, _ = _ref(False, inp)
+    assert rel_l2(o, o_ref) <= TOL_BF16 and rel_l2(sf, s_ref) <= TOL_BF16
+    e = synth.make_prefill(1, 2, 0, 128, 128, torch.bfloat16, s0_std=0.01, seed=4)
+    o, sf, _ = _gpu(False, e)
+    assert o.shape == (1, 2, 0, 128) and torch.equal(sf.cpu(), e["s0"])
+
+
+def test_gdn_mfma_in_place_and_deterministic():
+    import gated_deltanet_state_amd as g
+    say("mfma gdn in-place/determinism")
+    inp = synth.make_prefill(2, 4, 300, 128, 128, torch.bfloat16, s0_std=0.01, seed=5)
+    d = {k: v.cuda() for k, v in inp.items()}
+    args = [d[k] for k in ("q", "k", "v", "beta", "log_alpha")]
+    o1, s1, _ = g.gdn_chunk_fwd(*args, d["s0"], chunk=64)
+    o2, s2, _ = g.gdn_chunk_fwd(*args, d["s0"], chunk=64)
+    s = d["s0"].clone()
+    o3, _, _ = g.gdn_chunk_fwd(*args, s, chunk=64, s_final=s)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)       # bitwise run to run
+    assert torch.equal(o1, o3) and torch.equal(s1, s)        # in place == out of place
+
+
+def test_gdn_mfma_snapshots_and_resume():
+    import gated_deltanet_state_amd as g
+    say("mfma gdn snapshots/resume")
+    T, every = 640, 128
+    inp = synth.make_prefill(1, 2, T, 128, 128, torch.bfloat16, s0_std=0.01, seed=6)
+    o, sf, sc = _gpu(False, inp, ckpt_every=every, out_dtype=torch.float32)
+    o_ref, s_ref, c_ref = _ref(False, inp, ckpt_every=every)
+    assert sc.shape == (1, 2, 5, 128, 128)
+    assert rel_l2(sc, c_ref) <= TOL_BF16
+    assert torch.equal(sc[:, :, -1], sf)
+    # resume from snapshot 2 (after token 384): identical chunk alignment -> bitwise equal
+    tail = {k: (v[:, :, 384:].contiguous() if k != "s0" else None) for k, v in inp.items()}
+    tail["s0"] = sc[:, :, 2].cpu()
+    o2, sf2, _ = _gpu(False, tail, out_dtype=torch.float32)
+    assert torch.equal(o2, o[:, :, 384:]) and torch.equal(sf2, sf)
+
+
+def test_gdn_mfma_matches_decode_steps():
+    """T decode steps and one prefill agree (within the bf16 tolerance)."""
+    import gated_deltanet_state_amd as g
+    say("mfma gdn vs decode steps")
+    T = 96
+    inp = synth.make_prefill(1, 2, T, 128, 128, torch.bfloat16, s0_std=0.01, seed=7)
+    o, sf, _ = _gpu(False, inp, out_dtype=torch.float32)
+    st = inp["s0"].cuda().clone()
+    outs = []
+    for t in range(T):
+        outs.append(g.gdn_decode_step(st, *(inp[k][:, :, t].contiguous().cuda()
+                                            for k in ("q", "k", "v", "beta", "log_alpha")),
+                                      out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    od = torch.stack(outs, 2)
+    assert rel_l2(o, od) <= TOL_BF16 and rel_l2(sf, st) <= TOL_BF16
+
+
+def test_workload_prefill_full_size():
+    """B=4, H=16, T=4096, d=128, chunk 64, bf16; S0 = 0.01 N(0,1): all outputs and final states."""
+    c = synth.WORKLOADS[1]
+    say("prefill workload B=4 H=16 T=4096")
+    inp = synth.make_workload(1)
+    o, sf, _ = _gpu(False, inp)
+    o_ref, s_ref, _ = _ref(False, inp)
+    eo, es = rel_l2(o, o_ref), rel_l2(sf, s_ref)
+    print(f"prefill workload rel-L2 o={eo:.3e} s_final={es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_workload_long_prefill_snapshots_sampled_heads():
+    """B=1, H=32, T=65536 with a snapshot every 8192 tokens: the oracle follows 3 sampled
+    heads through the whole sequence (heads are independent); snapshot 8 equals the final
+    state bitwise."""
+    c = synth.WORKLOADS[2]
+    say("long prefill workload H=32 T=65536, 8 snapshots")
+    inp = synth.make_workload(2)
+    o, sf, sc = _gpu(False, inp, ckpt_every=c.ckpt_every)
+    assert sc.shape == (1, 32, 8, 128, 128)
+    assert torch.equal(sc[:, :, -1], sf)
+    heads = [0, 13, 31]
+    sub = {k: (v[:, heads].contiguous() if v is not None else None) for k, v in inp.items()}
+    o_ref, s_ref, c_ref = _ref(False, sub, ckpt_every=c.ckpt_every)
+    eo = rel_l2(o[:, heads], o_ref)
+    es = rel_l2(sf[:, heads], s_ref)
+    ec = rel_l2(sc[:, heads], c_ref)
+    print(f"long prefill rel-L2 o={eo:.3e} s_final={es:.3e} snapshots={ec:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16 and ec <= TOL_BF16
