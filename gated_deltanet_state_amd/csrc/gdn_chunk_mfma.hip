@@ -42,6 +42,7 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;       // head dimension (d_k = d_v)
 constexpr int C = 64;        // chunk length
@@ -80,6 +81,14 @@ __device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
+// Returns x unchanged but opaque to the optimiser, so per-lane addresses derived from it are
+// recomputed where they are used instead of being hoisted out of the chunk loop and kept
+// live across every phase (which would exhaust the 256 architectural registers).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Operand fragment of a 16 x 32 slice (rows m0.., columns k0..) of a row-major fp16 matrix:
 // lane l holds row m0 + l%16, columns k0 + 8*(l/16) .. +7.  Used for both MFMA operands
 // (for B the "rows" are the N index).
@@ -91,6 +100,11 @@ __device__ __forceinline__ h4 frag4(const _Float16* base, int ld, int m0, int k0
   return *reinterpret_cast<const h4*>(base + (m0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
 }
 
+// The transposed-key tile kt[d_k][token] stores its 16-byte groups of 8 tokens XOR-swizzled
+// by bits 3..5 of the key channel, so that the staging writes (16 lanes writing 16 channels
+// 8 apart, same tokens) spread over the LDS banks; 16-byte reads stay contiguous.
+__device__ __forceinline__ int kt_col(int dk, int c) { return (((c >> 3) ^ ((dk >> 3) & 7)) << 3) | (c & 7); }
+
 __device__ __forceinline__ h4 to_h4(f4 x) {
   h4 r;
   r[0] = (_Float16)x[0]; r[1] = (_Float16)x[1]; r[2] = (_Float16)x[2]; r[3] = (_Float16)x[3];
@@ -98,8 +112,8 @@ __device__ __forceinline__ h4 to_h4(f4 x) {
 }
 
 // 8 bf16 (packed in 4 dwords, element 2i in the low half) -> 8 fp16 (exact for |x| <= 65504)
-__device__ __forceinline__ h8 bf8_to_h8(uint4 x) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+__device__ __forceinline__ h8 bf8_to_h8(v4u x) {
+  const uint32_t w[4] = {x[0], x[1], x[2], x[3]};
   h8 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -115,37 +129,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return lo | (hi << 16);
 }
 
-// Global -> register staging of one chunk's inputs.
-struct Stage {
-  uint4 q[4], k[4];  // rows 4*(tid/16)+i, channels 8*(tid%16)..+7
-  uint4 v;           // row tid/4, value channels c0 + 8*(tid%4)..+7
-  float beta, g;     // token tid (threads 0..63)
+// Global -> register staging of one chunk's inputs, through buffer loads on per-stream
+// buffer descriptors: the hardware range check returns zeros for tokens at or past the end
+// of the stream, which pads a ragged last chunk with identity steps (k = v = q = 0,
+// beta = 0, log alpha = 0) without branches, and buffer loads never touch the LDS
+// counter, so waits on LDS traffic never wait for the prefetch.
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer: 32-bit dwords, no swizzle
+
+struct Streams {
+  __amdgpu_buffer_rsrc_t q, k, v, beta, g;
 };
 
-__device__ __forceinline__ float bf_at(const uint16_t* p, int64_t i) {
-  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+__device__ __forceinline__ Streams make_streams(const ChunkArgs& p, int64_t bh) {
+  const int64_t tok = bh * p.T;
+  const int bytes_qkv = (int)(p.T * D * 2);
+  const int bytes_tok = (int)(p.T * 2);
+  Streams s;
+  s.q = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.q + tok * D), 0, bytes_qkv, kRsrcWord3);
+  s.k = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.k + tok * D), 0, bytes_qkv, kRsrcWord3);
+  s.v = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.v + tok * D), 0, bytes_qkv, kRsrcWord3);
+  s.beta = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.beta + tok), 0, bytes_tok, kRsrcWord3);
+  s.g = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.log_alpha + tok), 0, bytes_tok, kRsrcWord3);
+  return s;
 }
 
-__device__ __forceinline__ void stage_load(Stage& st, const ChunkArgs& p, int64_t bh, int64_t t0, int n,
-                                           int tid, int c0) {
-  const uint4* Q = static_cast<const uint4*>(p.q);
-  const uint4* K = static_cast<const uint4*>(p.k);
-  const uint4* V = static_cast<const uint4*>(p.v);
+struct Stage {
+  v4u q[4], k[4];      // rows 4*(tid/16)+i, channels 8*(tid%16)..+7 (bf16 pairs)
+  v4u v;               // row tid/4, value channels c0 + 8*(tid%4)..+7
+  unsigned short beta, g;  // token tid (threads 0..63)
+};
+
+__device__ __forceinline__ void stage_load(Stage& st, const Streams& sr, int64_t t0, int tid, int c0) {
   const int g8 = tid & 15, rq = tid >> 4;
-  const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = 4 * rq + i;
-    const int64_t off = ((bh * p.T + t0 + row) * D) / 8 + g8;  // in uint4 units
-    st.q[i] = row < n ? Q[off] : z;
-    st.k[i] = row < n ? K[off] : z;
+    const int off = (int)(((t0 + 4 * rq + i) * D + 8 * g8) * 2);
+    st.q[i] = __builtin_amdgcn_raw_buffer_load_b128(sr.q, off, 0, 0);
+    st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(sr.k, off, 0, 0);
   }
-  const int vrow = tid >> 2;
-  st.v = vrow < n ? V[((bh * p.T + t0 + vrow) * D + c0) / 8 + (tid & 3)] : z;
+  st.v = __builtin_amdgcn_raw_buffer_load_b128(sr.v, (int)(((t0 + (tid >> 2)) * D + c0 + 8 * (tid & 3)) * 2), 0, 0);
   if (tid < C) {
-    const bool in = tid < n;
-    st.beta = in ? bf_at(static_cast<const uint16_t*>(p.beta), bh * p.T + t0 + tid) : 0.f;
-    st.g = in ? bf_at(static_cast<const uint16_t*>(p.log_alpha), bh * p.T + t0 + tid) : 0.f;
+    st.beta = __builtin_amdgcn_raw_buffer_load_b16(sr.beta, (int)((t0 + tid) * 2), 0, 0);
+    st.g = __builtin_amdgcn_raw_buffer_load_b16(sr.g, (int)((t0 + tid) * 2), 0, 0);
   }
 }
 
@@ -164,12 +189,12 @@ __device__ __forceinline__ void stage_store(const Stage& st, Smem& sm, int tid) 
   for (int e = 0; e < 8; ++e) {
     h4 col;
     col[0] = kh[0][e]; col[1] = kh[1][e]; col[2] = kh[2][e]; col[3] = kh[3][e];
-    *reinterpret_cast<h4*>(&sm.kt[8 * g8 + e][4 * rq]) = col;
+    *reinterpret_cast<h4*>(&sm.kt[8 * g8 + e][kt_col(8 * g8 + e, 4 * rq)]) = col;
   }
   *reinterpret_cast<h8*>(&sm.v[tid >> 2][8 * (tid & 3)]) = bf8_to_h8(st.v);
   if (tid < C) {
     // wavefront 0: inclusive prefix sum of log alpha over the 64 tokens
-    float x = st.g;
+    float x = __uint_as_float(static_cast<uint32_t>(st.g) << 16);
 #pragma unroll
     for (int off = 1; off < C; off <<= 1) {
       const float y = __shfl_up(x, off, 64);
@@ -182,7 +207,7 @@ __device__ __forceinline__ void stage_store(const Stage& st, Smem& sm, int tid) 
     sm.G[tid] = x;
     sm.gam[tid] = __expf(x);
     sm.dec[tid] = __expf(glast - x);
-    sm.beta[tid] = st.beta;
+    sm.beta[tid] = __uint_as_float(static_cast<uint32_t>(st.beta) << 16);
     sm.el[tid] = __expf(x - gref);
     sm.er[1][tid] = tid < 16 ? __expf(gr1 - x) : 0.f;
     sm.er[2][tid] = tid < 32 ? __expf(gr2 - x) : 0.f;
@@ -190,14 +215,96 @@ __device__ __forceinline__ void stage_store(const Stage& st, Smem& sm, int tid) 
   }
 }
 
-// Gram-tile jobs (kind, R, J): kind 0 -> A block (R, J) from K K^T, kind 1 -> P block from Q K^T.
-// Each wavefront takes two diagonal jobs and three off-diagonal ones.
-constexpr unsigned char job(int kind, int R, int J) { return (unsigned char)((kind << 4) | (R << 2) | J); }
-__device__ __constant__ unsigned char kJobs[4][5] = {
-    {job(0, 0, 0), job(1, 1, 1), job(0, 1, 0), job(0, 3, 1), job(1, 2, 1)},
-    {job(0, 1, 1), job(1, 3, 3), job(0, 2, 0), job(0, 3, 2), job(1, 3, 0)},
-    {job(0, 2, 2), job(1, 0, 0), job(0, 2, 1), job(1, 1, 0), job(1, 3, 1)},
-    {job(0, 3, 3), job(1, 2, 2), job(0, 3, 0), job(1, 2, 0), job(1, 3, 2)}};
+// Epilogue of one Gram tile held as (M = j, N = r): lane holds j = 16 J + 4 lg + i, r = 16 R + lr.
+// KIND 0: A block -> fp32 diagonal block or fp16 -A off the diagonal; KIND 1: P block (fp16).
+template <int KIND>
+__device__ __forceinline__ void gram_epilogue(Smem& sm, int R, int J, int lr, int lg, f4 acc) {
+  const int r = 16 * R + lr, j0 = 16 * J + 4 * lg;
+  f4 f;
+  if (R == J) {
+    const float gr = sm.G[r];
+    const f4 gj = *reinterpret_cast<const f4*>(&sm.G[j0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + i;
+      const bool keep = KIND ? (j <= r) : (j < r);
+      const float e = __expf(fminf(gr - gj[i], 0.f));  // <= 1; masked entries are dropped below
+      f[i] = keep ? e : 0.f;
+    }
+  } else {
+    f = sm.el[r] * *reinterpret_cast<const f4*>(&sm.er[R][j0]);
+  }
+  if (KIND == 0) {
+    const f4 a = (sm.beta[r] * f) * acc;
+    if (R == J)
+      *reinterpret_cast<f4*>(&sm.ad[R][lr][4 * lg]) = a;
+    else
+      *reinterpret_cast<h4*>(&sm.an[r][j0]) = to_h4(-a);
+  } else {
+    *reinterpret_cast<h4*>(&sm.p[r][j0]) = to_h4(f * acc);
+  }
+}
+
+// Column block J of A and P: tiles (R, J), R = J..3.  The key fragment of block J is loaded
+// once per 32-channel step and reused by all 2 (4 - J) tiles of the column.
+template <int J>
+__device__ __forceinline__ void gram_column(Smem& sm, int l, int lr, int lg) {
+  constexpr int NR = 4 - J;
+  f4 accA[NR], accP[NR];
+#pragma unroll
+  for (int t = 0; t < NR; ++t) {
+    accA[t] = f4{0.f, 0.f, 0.f, 0.f};
+    accP[t] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const h8 a = frag8(&sm.k[0][0], LQ, 16 * J, 32 * kk, l);
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+      accA[t] = mfma32(a, frag8(&sm.k[0][0], LQ, 16 * (J + t), 32 * kk, l), accA[t]);
+      accP[t] = mfma32(a, frag8(&sm.q[0][0], LQ, 16 * (J + t), 32 * kk, l), accP[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NR; ++t) {
+    gram_epilogue<0>(sm, J + t, J, lr, lg, accA[t]);
+    gram_epilogue<1>(sm, J + t, J, lr, lg, accP[t]);
+  }
+}
+
+// Inverse of the unit lower-triangular diagonal block (I + A_JJ) by fp32 forward
+// substitution, T[r][n] = delta_rn - sum_{j<r} A[r][j] T[j][n]; lane n < 16 owns column n
+// (entries above the diagonal come out zero because T[j][n] = 0 for j < n).  Called by the
+// wavefront that wrote A_JJ, so its own LDS writes are already ordered before these reads.
+__device__ __forceinline__ void invert_diag(Smem& sm, int J, int l) {
+  if (l < 16) {
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float arow[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f4 x = *reinterpret_cast<const f4*>(&sm.ad[J][r][4 * q]);
+        arow[4 * q] = x[0]; arow[4 * q + 1] = x[1]; arow[4 * q + 2] = x[2]; arow[4 * q + 3] = x[3];
+      }
+      float acc = (r == l) ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < r; ++j) acc -= arow[j] * t[j];
+      t[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm.td[J][r][l] = (_Float16)t[r];
+  }
+}
+
+// Output tiles O^T (token block cb, value block db) owned by wavefront w: w even owns one,
+// w odd three, so that every wavefront issues the same number of products in phase 1.
+__device__ __forceinline__ int o_tiles(int w) { return (w & 1) ? 3 : 1; }
+__device__ __forceinline__ void o_tile(int w, int t, int& cb, int& db) {
+  const int idx = (w & 1) ? t + 1 : 0;
+  cb = 2 * (w >> 1) + (idx >> 1);
+  db = idx & 1;
+}
 
 template <typename TOut>
 __device__ __forceinline__ void store_o4(TOut* o, int64_t idx, f4 x);
@@ -217,8 +324,9 @@ template <typename TOut>
 __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63;
-  const int lr = l & 15, lg = l >> 4;  // lane row / lane group in MFMA layouts
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int l = tid & 63;
+  int lr = l & 15, lg = l >> 4;  // lane row / lane group in MFMA layouts
 
   // XCD-aware placement: consecutive workgroup ids are dealt round-robin over the 8 XCDs;
   // remap so the NT slices of a stream get ids that land on the same XCD.
@@ -251,9 +359,10 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
       *reinterpret_cast<h4*>(&sm.s[dv][dk]) = to_h4(x);
     }
 
+  const Streams sr = make_streams(p, bh);
   Stage st;
   if (nchunks > 0) {
-    stage_load(st, p, bh, 0, (int)(T < C ? T : C), tid, c0);
+    stage_load(st, sr, 0, tid, c0);
     stage_store(st, sm, tid);
   }
   __syncthreads();
@@ -263,105 +372,57 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
     const int64_t t0 = ci * C;
     const int n = (int)(T - t0 < C ? T - t0 : C);
     const bool more = ci + 1 < nchunks;
-    if (more) {
-      const int64_t t1 = t0 + C;
-      stage_load(st, p, bh, t1, (int)(T - t1 < C ? T - t1 : C), tid, c0);
-    }
+    if (more) stage_load(st, sr, t0 + C, tid, c0);
 
-    // ---- phase 1: Gram tiles, X = diag(beta)(V - diag(gamma) K S^T), O = diag(gamma) Q S^T
-#pragma unroll
-    for (int jb = 0; jb < 5; ++jb) {
-      const int job = kJobs[w][jb];
-      const int kind = job >> 4, R = (job >> 2) & 3, J = job & 3;
-      const _Float16* Bm = kind ? &sm.q[0][0] : &sm.k[0][0];
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        acc = mfma32(frag8(&sm.k[0][0], LQ, 16 * J, 32 * kk, l), frag8(Bm, LQ, 16 * R, 32 * kk, l), acc);
-      // lane holds (M = j, N = r): j = 16 J + 4 lg + i, r = 16 R + lr
-      const int r = 16 * R + lr, j0 = 16 * J + 4 * lg;
-      f4 f;
-      if (R == J) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = j0 + i;
-          const bool keep = kind ? (j <= r) : (j < r);
-          f[i] = keep ? __expf(sm.G[r] - sm.G[j]) : 0.f;
-        }
-      } else {
-        const float el = sm.el[r];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = el * sm.er[R][j0 + i];
-      }
-      if (kind == 0) {
-        const float b = sm.beta[r];
-        f4 a;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = b * f[i] * acc[i];
-        if (R == J) {
-          *reinterpret_cast<f4*>(&sm.ad[R][lr][4 * lg]) = a;
-        } else {
-          *reinterpret_cast<h4*>(&sm.an[r][j0]) = to_h4(-a);
-        }
-      } else {
-        *reinterpret_cast<h4*>(&sm.p[r][j0]) = to_h4(f * acc);
-      }
+    // ---- phase 1: Gram column J = w, value tiles X (waves 2, 3), O = diag(gamma) Q S^T tiles,
+    // then the inverse of the diagonal block (I + A_ww)
+    l = opaque(l), lr = l & 15, lg = l >> 4;
+    switch (w) {
+      case 0: gram_column<0>(sm, l, lr, lg); break;
+      case 1: gram_column<1>(sm, l, lr, lg); break;
+      case 2: gram_column<2>(sm, l, lr, lg); break;
+      default: gram_column<3>(sm, l, lr, lg); break;
     }
-
-    f4 X[4];       // waves 0,1: X tiles of value block db = w, token blocks 0..3
-    f4 Oacc[2][2]; // waves 2,3: O^T tiles, token blocks 2(w-2)+a, value blocks db
-    if (w < 2) {
-      const int db = w;
+    f4 X[4];
+    if (w >= 2) {
+      const int db = w - 2;
+      const int dv = 16 * db + lr;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           acc = mfma32(frag8(&sm.k[0][0], LQ, 16 * i, 32 * kk, l), frag8(&sm.s[0][0], LQ, 16 * db, 32 * kk, l), acc);
-        // lane: token c = 16 i + 4 lg + e, value channel dv = 16 db + lr
-        const int dv = 16 * db + lr;
+        // lane: token c = 16 i + 4 lg + e, value channel dv
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int c = 16 * i + 4 * lg + e;
           X[i][e] = sm.beta[c] * ((float)sm.v[c][dv] - sm.gam[c] * acc[e]);
         }
       }
-    } else {
+    }
+    f4 Oacc[3];
+    const int nO = o_tiles(w);
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int cb = 2 * (w - 2) + a;
+    for (int t = 0; t < 3; ++t) {
+      if (t < nO) {
+        int cb, db;
+        o_tile(w, t, cb, db);
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            acc = mfma32(frag8(&sm.s[0][0], LQ, 16 * db, 32 * kk, l), frag8(&sm.q[0][0], LQ, 16 * cb, 32 * kk, l), acc);
-          // lane: value channel dv = 16 db + 4 lg + e, token c = 16 cb + lr
-          Oacc[a][db] = acc * sm.gam[16 * cb + lr];
-        }
+        for (int kk = 0; kk < 4; ++kk)
+          acc = mfma32(frag8(&sm.s[0][0], LQ, 16 * db, 32 * kk, l), frag8(&sm.q[0][0], LQ, 16 * cb, 32 * kk, l), acc);
+        // lane: value channel dv = 16 db + 4 lg + e, token c = 16 cb + lr
+        Oacc[t] = acc * sm.gam[16 * cb + lr];
       }
     }
+    invert_diag(sm, w, l);
     __syncthreads();
 
-    // ---- phase 2: invert the 16x16 diagonal blocks of (I + A), fp32 forward substitution;
-    // wavefront w takes block w, lane n < 16 owns column n.
-    if (l < 16) {
-      float t[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == l) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < r; ++j) acc -= sm.ad[w][r][j] * t[j];
-        t[r] = acc;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sm.td[w][r][l] = (_Float16)t[r];
-    }
-    __syncthreads();
-
-    // ---- phase 3: block forward substitution U_i = T_ii (X_i - sum_{j<i} A_ij U_j)
-    if (w < 2) {
-      const int db = w;
+    // ---- phase 3: block forward substitution U_i = T_ii (X_i - sum_{j<i} A_ij U_j), waves 2, 3
+    l = opaque(l), lr = l & 15, lg = l >> 4;
+    if (w >= 2) {
+      const int db = w - 2;
       const int dv = 16 * db + lr;
       h4 Uh[4];
 #pragma unroll
@@ -383,24 +444,20 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
     }
     __syncthreads();
 
-    // ---- phase 4: O += U^T P^T (waves 2,3) and the state hand-off (all waves)
-    if (w >= 2) {
+    // ---- phase 4: O += U^T P^T on the owned output tiles, then the state hand-off
+    l = opaque(l), lr = l & 15, lg = l >> 4;
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int cb = 2 * (w - 2) + a;
+    for (int t = 0; t < 3; ++t) {
+      if (t < nO) {
+        int cb, db;
+        o_tile(w, t, cb, db);
+        f4 acc = Oacc[t];
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          f4 acc = Oacc[a][db];
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc)
-            if (kc == 0 || cb >= 2)
-              acc = mfma32(frag8(&sm.u[0][0], LC, 16 * db, 32 * kc, l), frag8(&sm.p[0][0], LC, 16 * cb, 32 * kc, l), acc);
-          const int c = 16 * cb + lr;
-          if (c < n) {
-            const int dv = 16 * db + 4 * lg;
-            store_o4<TOut>(O, (bh * T + t0 + c) * D + c0 + dv, acc);
-          }
-        }
+        for (int kc = 0; kc < 2; ++kc)
+          if (kc == 0 || cb >= 2)
+            acc = mfma32(frag8(&sm.u[0][0], LC, 16 * db, 32 * kc, l), frag8(&sm.p[0][0], LC, 16 * cb, 32 * kc, l), acc);
+        const int c = 16 * cb + lr;
+        if (c < n) store_o4<TOut>(O, (bh * T + t0 + c) * D + c0 + 16 * db + 4 * lg, acc);
       }
     }
     const float glast = sm.gam[C - 1];
@@ -410,10 +467,13 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const int kb = 2 * w + a;
+        const int dkr = 16 * kb + lr;  // key channel of this lane's A-operand row
         f4 acc = S[a][db] * glast;
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-          acc = mfma32(frag8(&sm.kt[0][0], LC, 16 * kb, 32 * kc, l), frag8(&sm.ud[0][0], LC, 16 * db, 32 * kc, l), acc);
+        for (int kc = 0; kc < 2; ++kc) {
+          const h8 ka = *reinterpret_cast<const h8*>(&sm.kt[dkr][kt_col(dkr, 32 * kc + 8 * lg)]);
+          acc = mfma32(ka, frag8(&sm.ud[0][0], LC, 16 * db, 32 * kc, l), acc);
+        }
         S[a][db] = acc;
         const int dk = 16 * kb + 4 * lg, dv = 16 * db + lr;
         *reinterpret_cast<h4*>(&sm.s[dv][dk]) = to_h4(acc);
@@ -443,7 +503,8 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
 }  // namespace
 
 bool chunk_mfma_supported(const ChunkArgs& a) {
-  return a.in_dtype == GDN_BF16 && a.D == D && a.chunk == C;
+  // buffer-descriptor offsets are 32-bit: one stream's q/k/v must stay under 2 GiB
+  return a.in_dtype == GDN_BF16 && a.D == D && a.chunk == C && a.T * D * 2 < (INT64_C(1) << 31);
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool kda, hipStream_t s) {
