@@ -9,7 +9,7 @@ import time
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_chunk_valu.hip", "gdn_chunk_mfma.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_chunk_valu.hip", "gdn_chunk_mfma.hip", "kda_chunk_mfma.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -38,14 +38,12 @@
 #include <hip/hip_bf16.h>
 
 #include "gdn_internal.h"
+#include "gdn_mfma_common.h"
 
 namespace gdn {
 namespace {
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
+using namespace mfma;
 
 constexpr int D = 128;       // head dimension (d_k = d_v)
 constexpr int C = 64;        // chunk length
@@ -81,88 +79,12 @@ struct alignas(16) Smem {
   alignas(16) Gates gt[2];
 };
 
-__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-
-// Returns x unchanged but opaque to the optimiser, so per-lane addresses derived from it are
-// recomputed where they are used instead of being hoisted out of the chunk loop and kept
-// live across every phase.
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-// Operand fragment of a 16 x 32 slice (rows m0.., columns k0..) of a row-major fp16 matrix:
-// lane l holds row m0 + l%16, columns k0 + 8*(l/16) .. +7.  Used for both MFMA operands
-// (for B the "rows" are the N index).
-__device__ __forceinline__ h8 frag8(const _Float16* base, int ld, int m0, int k0, int lane) {
-  return *reinterpret_cast<const h8*>(base + (m0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
-}
-// Same for a 16 x 16 slice and the 16x16x16 instruction: columns k0 + 4*(l/16) .. +3.
-__device__ __forceinline__ h4 frag4(const _Float16* base, int ld, int m0, int k0, int lane) {
-  return *reinterpret_cast<const h4*>(base + (m0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
-}
-
-// The transposed-key tile kt[d_k][token] stores its 16-byte groups of 8 tokens XOR-swizzled
-// by bits 3..5 of the key channel, so that the staging writes (16 lanes writing 16 channels
-// 8 apart, same tokens) spread over the LDS banks; 16-byte reads stay contiguous.
-__device__ __forceinline__ int kt_col(int dk, int c) { return (((c >> 3) ^ ((dk >> 3) & 7)) << 3) | (c & 7); }
-
-__device__ __forceinline__ h4 to_h4(f4 x) {
-  h4 r;
-  r[0] = (_Float16)x[0]; r[1] = (_Float16)x[1]; r[2] = (_Float16)x[2]; r[3] = (_Float16)x[3];
-  return r;
-}
-
-// 8 bf16 (packed in 4 dwords, element 2i in the low half) -> 8 fp16.  bf16 -> fp16 is exact
-// for |x| in [2^-14, 65504] (8 significant bits fit in 11), so the round-toward-zero packed
-// conversion gives the same bits as round-to-nearest at 3 instructions per pair.
-__device__ __forceinline__ h8 bf8_to_h8(v4u x) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  h8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const h2 pr = __builtin_bit_cast(
-        h2, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(x[i] << 16), __uint_as_float(x[i] & 0xffff0000u)));
-    r[2 * i] = pr[0];
-    r[2 * i + 1] = pr[1];
-  }
-  return r;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const uint32_t lo = __bfloat16_as_ushort(__float2bfloat16(a));
-  const uint32_t hi = __bfloat16_as_ushort(__float2bfloat16(b));
-  return lo | (hi << 16);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wavefront with DPP: shifts within rows of 16
-// lanes, then the row broadcasts of lane 15 and lane 31.
-__device__ __forceinline__ float wave_prefix_sum(float x) {
-  int v = __float_as_int(x);
-#define GDN_DPP_STEP(ctrl, rows) \
-  v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, ctrl, rows, 0xf, false)))
-  GDN_DPP_STEP(0x111, 0xf);  // row_shr:1
-  GDN_DPP_STEP(0x112, 0xf);  // row_shr:2
-  GDN_DPP_STEP(0x114, 0xf);  // row_shr:4
-  GDN_DPP_STEP(0x118, 0xf);  // row_shr:8
-  GDN_DPP_STEP(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
-  GDN_DPP_STEP(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
-#undef GDN_DPP_STEP
-  return __int_as_float(v);
-}
-
 // ------------------------------------------------------------------------------------------
 // Staging.  Global -> registers through buffer loads on per-stream buffer descriptors: the
 // hardware range check returns zeros for tokens at or past the end of the stream, which pads
 // a ragged last chunk with identity steps (k = v = q = 0, beta = 0, log alpha = 0) without
 // branches, and buffer loads never touch the LDS counter, so waits on LDS traffic never wait
 // for the prefetch.  Threads 0..255 stage keys (and values, gates), threads 256..511 queries.
-constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer: 32-bit dwords, no swizzle
 
 struct Streams {
   __amdgpu_buffer_rsrc_t qk, v, beta, g;
@@ -344,20 +266,6 @@ __device__ __forceinline__ void produce(Smem& sm, int b, int w, int l) {
     case 6: gram_jobs<job(1, 3, 2), job(0, 3, 3), kNone, kNone>(sm, b, l); break;
     default: gram_jobs<job(1, 2, 2), job(0, 3, 2), job(1, 3, 3), kNone>(sm, b, l); break;
   }
-}
-
-template <typename TOut>
-__device__ __forceinline__ void store_o4(TOut* o, int64_t idx, f4 x);
-template <>
-__device__ __forceinline__ void store_o4<float>(float* o, int64_t idx, f4 x) {
-  *reinterpret_cast<f4*>(o + idx) = x;
-}
-template <>
-__device__ __forceinline__ void store_o4<__hip_bfloat16>(__hip_bfloat16* o, int64_t idx, f4 x) {
-  uint2 w;
-  w.x = pack_bf16x2(x[0], x[1]);
-  w.y = pack_bf16x2(x[2], x[3]);
-  *reinterpret_cast<uint2*>(o + idx) = w;
 }
 
 template <typename TOut>
@@ -555,7 +463,7 @@ bool chunk_mfma_supported(const ChunkArgs& a) {
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool kda, hipStream_t s) {
-  if (kda) return launch_chunk_valu(a, true, s);  // per-channel decay: vector path for now
+  if (kda) return launch_kda_mfma(a, s);
   const int64_t blocks = a.B * a.H * NT;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (a.out_dtype == GDN_BF16)

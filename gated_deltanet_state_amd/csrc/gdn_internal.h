@@ -34,6 +34,7 @@ struct DecodeArgs {
 // Matrix-core prefill (bf16 inputs, D = 128, chunk = 64).
 bool chunk_mfma_supported(const ChunkArgs& a);
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool kda, hipStream_t stream);
+hipError_t launch_kda_mfma(const ChunkArgs& a, hipStream_t stream);
 
 // fp32 vector-unit prefill (fp32 or bf16 inputs, D in {16,32,64,128}, chunk in {16,32,64}).
 bool chunk_valu_supported(const ChunkArgs& a);

@@ -1,0 +1,513 @@
+// kda_chunk_mfma.hip -- matrix-core chunkwise prefill of KDA (per-channel decay) for gfx950
+// (bf16 inputs, d_k = d_v = 128, chunk = 64, fp32 state and accumulation).
+//
+// KDA replaces the scalar gate of the gated delta rule by one forget rate per key channel,
+// S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T ("From Traditional
+// Attention to hybrid ones", section 7).  Its chunkwise form ("Hybrid Linear Attention
+// Architecture Design Explained", section 4) in the d_v x d_k convention, with the
+// per-channel prefix G_r = sum_{s<=r} log alpha_s in R^{d_k} and Gamma_r = e^{G_r}:
+//   A = strict_tril(diag(beta) (K*Gamma)(K/Gamma)^T),  X = diag(beta)(V - (K*Gamma) S^T)
+//   (I + A) U = X
+//   O = (Q*Gamma) S^T + tril((Q*Gamma)(K/Gamma)^T) U
+//   S <- S Diag(Gamma_63) + U^T (K * e^{G_63 - G})
+// The page notes that the division form needs overflow protection.  Here every factor
+// e^{G_r - G_j} (j <= r, always <= 1) is split at a reference point between j and r so that
+// both half-precision operands stay bounded:
+//   * off the diagonal 16-token blocks (j in block J < R = block of r) the split point is the
+//     end of block J: (k_r e^{G_r - G_end(J)}) . (k_j e^{G_end(J) - G_j}), both factors <= 1
+//     for any gate strength;
+//   * inside a diagonal block the split point is its middle token m: factors are bounded by
+//     e^{8 max|log alpha|}, which stays in half range while the log-gates of 8 consecutive
+//     tokens sum to more than -11 in every channel (documented precondition of this path).
+// Work decomposition as in the scalar-gate kernel (a workgroup per stream and 32 value rows,
+// 8 wavefronts), without its cross-chunk pipelining: the per-channel operand tiles fill the
+// LDS.  Per chunk: stage (log-gate prefix per channel, scaled operand tiles) | Gram/score
+// tiles, diagonal inverses, X, O | substitution | O += P U and the state hand-off.
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+
+#include "gdn_internal.h"
+#include "gdn_mfma_common.h"
+
+namespace gdn {
+namespace {
+
+using namespace mfma;
+
+constexpr int D = 128;       // head dimension (d_k = d_v)
+constexpr int C = 64;        // chunk length
+constexpr int DVT = 32;      // value rows per workgroup
+constexpr int NT = D / DVT;  // workgroups per stream
+constexpr int NTH = 512;     // threads per workgroup
+constexpr int LQ = D + 8;    // row stride (halves) of [token][channel] tiles
+constexpr int LC = C + 8;    // row stride (halves) of [channel][token] and [token][token] tiles
+constexpr int LT = 24;       // row stride (halves) of 16x16 blocks
+constexpr int LG = D + 4;    // row stride (floats) of the fp32 prefix G[token][channel]
+
+struct alignas(16) Tables {
+  alignas(16) float beta[C];
+  alignas(16) float em[4][D];     // e^{G_m(R)}, m(R) = 16 R + 7: turns k e^{G - G_m} into k e^{G}
+  alignas(16) float fm[4][4][D];  // fm[R][J] = e^{G_m(R) - G_end(J)}, J < R, G_end(J) = G_{16J+15}
+  alignas(16) float gc[D];        // e^{G_63}
+};
+
+struct alignas(16) Products {
+  alignas(16) _Float16 p[C][LC];        // tril((Q*Gamma)(K/Gamma)^T), inclusive
+  alignas(16) _Float16 an[C][LC];       // -A, off-diagonal 16x16 blocks
+  alignas(16) _Float16 td[4][16][LT];   // inverses of the diagonal blocks of (I + A), row-major
+  alignas(16) _Float16 nt[4][16][LT];   // scratch: transposed diagonal blocks of A
+  alignas(16) _Float16 u[DVT][LC];      // U [d_v][token]
+};
+
+struct alignas(16) Prefix {
+  alignas(16) float G[C][LG];           // inclusive prefix of log alpha per channel
+  alignas(16) float tot[16][D];         // sums over groups of 4 tokens
+};
+
+struct alignas(16) Smem {
+  alignas(16) _Float16 ql[C][LQ];   // q_r e^{G_r - G_m(R)}
+  alignas(16) _Float16 kl[C][LQ];   // k_r e^{G_r - G_m(R)}
+  alignas(16) _Float16 kd[C][LQ];   // k_j e^{G_m(J) - G_j}         (A operand, diagonal blocks)
+  alignas(16) _Float16 kr[C][LQ];   // k_j e^{G_end(J) - G_j} <= |k|  (A operand, off the diagonal)
+  alignas(16) _Float16 kt[D][LC];   // k_c e^{G_63 - G_c} <= |k|, transposed [d_k][token], swizzled
+  alignas(16) _Float16 s[DVT][LQ];  // fp16 copy of the state slice [d_v][d_k]
+  alignas(16) _Float16 v[C][DVT + 8];
+  union {                           // the prefix lives only while the chunk is staged
+    Prefix pf;
+    Products pr;
+  };
+  Tables tb;
+};
+
+struct Streams {
+  __amdgpu_buffer_rsrc_t qk, g, v, beta;
+};
+
+__device__ __forceinline__ Streams make_streams(const ChunkArgs& p, int64_t bh, bool is_q) {
+  const int64_t tok = bh * p.T;
+  const int bytes_qkv = (int)(p.T * D * 2);
+  Streams s;
+  s.qk = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)(is_q ? p.q : p.k) + tok * D), 0, bytes_qkv, kRsrcWord3);
+  s.g = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.log_alpha + tok * D), 0, bytes_qkv, kRsrcWord3);
+  s.v = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.v + tok * D), 0, bytes_qkv, kRsrcWord3);
+  s.beta = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.beta + tok), 0, (int)(p.T * 2), kRsrcWord3);
+  return s;
+}
+
+// Threads 0..255 stage keys, log-gates, values and beta; threads 256..511 queries.  Tokens
+// past the end of the stream read as zeros (identity steps).
+struct Stage {
+  v4u x[4];   // q or k: rows 4*(t/16)+i, channels 8*(t%16)..+7
+  v4u g[4];   // log alpha, same layout (key threads)
+  v4u v;      // key threads: row t/4, value channels c0 + 8*(t%4)..+7
+  unsigned short beta;
+};
+
+__device__ __forceinline__ void stage_load(Stage& st, const Streams& sr, int64_t t0, int tid, int c0) {
+  const int t = tid & 255, g8 = t & 15, rq = t >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int off = (int)(((t0 + 4 * rq + i) * D + 8 * g8) * 2);
+    st.x[i] = __builtin_amdgcn_raw_buffer_load_b128(sr.qk, off, 0, 0);
+    if (tid < 256) st.g[i] = __builtin_amdgcn_raw_buffer_load_b128(sr.g, off, 0, 0);
+  }
+  if (tid < 256)
+    st.v = __builtin_amdgcn_raw_buffer_load_b128(sr.v, (int)(((t0 + (t >> 2)) * D + c0 + 8 * (t & 3)) * 2), 0, 0);
+  if (tid < C) st.beta = __builtin_amdgcn_raw_buffer_load_b16(sr.beta, (int)((t0 + tid) * 2), 0, 0);
+}
+
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf_at(v4u x, int e) { return (e & 1) ? bf_hi(x[e >> 1]) : bf_lo(x[e >> 1]); }
+
+// Half-precision operand fragment (8 channels) scaled per channel by an fp32 table row,
+// rounded to nearest once.
+__device__ __forceinline__ h8 scale8(h8 a, const float* tab) {
+  const f4 t0 = *reinterpret_cast<const f4*>(tab), t1 = *reinterpret_cast<const f4*>(tab + 4);
+  h8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (_Float16)((float)a[i] * t0[i]);
+    r[4 + i] = (_Float16)((float)a[4 + i] * t1[i]);
+  }
+  return r;
+}
+
+// Inverse of (I + N), N = A_JJ strictly lower, on 16x16x16 MFMAs (see the scalar-gate kernel).
+__device__ __forceinline__ void invert_diag(Smem& sm, int J, f4 rowN, int lr, int lg) {
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  f4 eye;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) eye[i] = (4 * lg + i == lr) ? 1.f : 0.f;
+  const h4 rN = to_h4(rowN);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sm.pr.nt[J][4 * lg + i][lr] = rN[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const h4 cN = *reinterpret_cast<const h4*>(&sm.pr.nt[J][lr][4 * lg]);
+  const f4 n2c = mfma16(rN, cN, zero), n2r = mfma16(cN, rN, zero);
+  const h4 n2ch = to_h4(n2c), n2rh = to_h4(n2r);
+  const f4 n4c = mfma16(n2rh, n2ch, zero), n4r = mfma16(n2ch, n2rh, zero);
+  const f4 n8c = mfma16(to_h4(n4r), to_h4(n4c), zero);
+  const f4 p1r = mfma16(to_h4(n2c + eye), to_h4(eye - rowN), zero);
+  const f4 p2r = mfma16(to_h4(n4c + eye), to_h4(p1r), zero);
+  const f4 tr = mfma16(to_h4(n8c + eye), to_h4(p2r), zero);
+  *reinterpret_cast<h4*>(&sm.pr.td[J][lr][4 * lg]) = to_h4(tr);
+}
+
+// Job codes: kind << 4 | R << 2 | J.  kind 0: A tile (R, J); kind 1: P tile (R, J); kind 2:
+// output tile O^T (token block R, value block J), whose accumulator is kept for the P U step.
+constexpr int job(int kind, int R, int J) { return (kind << 4) | (R << 2) | J; }
+constexpr int kNone = -1;
+
+template <int J0, int J1, int J2, int J3, int J4>
+struct Jobs {
+  static constexpr int at[5] = {J0, J1, J2, J3, J4};
+};
+
+// Gram / score tile (M = j, N = r): the lane holds r = 16 R + lr, j = 16 J + 4 lg + i.
+template <class L>
+__device__ __forceinline__ void produce(Smem& sm, int l, f4* Oacc) {
+  const int lr = l & 15, lg = l >> 4;
+  f4 acc[5];
+#pragma unroll
+  for (int t = 0; t < 5; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int ch = 32 * kk + 8 * lg;  // channels of this lane's fragments
+#pragma unroll
+    for (int t = 0; t < 5; ++t) {
+      const int jb = L::at[t];
+      if (jb == kNone) continue;
+      const int kind = jb >> 4, R = (jb >> 2) & 3, J = jb & 3;
+      if (kind == 2) {  // O^T[dv][c] += sum S[dv][ch] (Q Gamma)[c][ch]: B operand = ql rows c * e^{G_m(R)}
+        const h8 qb = scale8(frag8(&sm.ql[0][0], LQ, 16 * R, 32 * kk, l), &sm.tb.em[R][ch]);
+        acc[t] = mfma32(frag8(&sm.s[0][0], LQ, 16 * J, 32 * kk, l), qb, acc[t]);
+      } else {
+        const _Float16* Am = (R == J) ? &sm.kd[0][0] : &sm.kr[0][0];
+        const _Float16* Bm = kind ? &sm.ql[0][0] : &sm.kl[0][0];
+        h8 b = frag8(Bm, LQ, 16 * R, 32 * kk, l);
+        if (R != J) b = scale8(b, &sm.tb.fm[R][J][ch]);
+        acc[t] = mfma32(frag8(Am, LQ, 16 * J, 32 * kk, l), b, acc[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0, no = 0; t < 5; ++t) {
+    const int jb = L::at[t];
+    if (jb == kNone) continue;
+    const int kind = jb >> 4, R = (jb >> 2) & 3, J = jb & 3;
+    if (kind == 2) {
+      Oacc[no++] = acc[t];
+      continue;
+    }
+    const int r = 16 * R + lr, j0 = 16 * J + 4 * lg;
+    f4 a = acc[t];
+    if (R == J) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + i;
+        if (kind ? (j > r) : (j >= r)) a[i] = 0.f;
+      }
+    }
+    if (kind == 1) {
+      *reinterpret_cast<h4*>(&sm.pr.p[r][j0]) = to_h4(a);
+    } else {
+      a *= sm.tb.beta[r];
+      if (R == J)
+        invert_diag(sm, J, a, lr, lg);
+      else
+        *reinterpret_cast<h4*>(&sm.pr.an[r][j0]) = to_h4(-a);
+    }
+  }
+}
+
+// Producer wavefronts 2..7: 20 A / P tiles (with the four diagonal inverses) and the 8 output
+// tiles; the O tiles of a wavefront are (R, J) = (token block, value block).
+using JobsW2 = Jobs<job(0, 0, 0), job(0, 1, 0), job(0, 2, 0), job(0, 3, 0), job(2, 0, 0)>;
+using JobsW3 = Jobs<job(1, 0, 0), job(1, 1, 0), job(1, 2, 0), job(1, 3, 0), job(2, 0, 1)>;
+using JobsW4 = Jobs<job(0, 1, 1), job(0, 2, 1), job(0, 3, 1), job(1, 1, 1), job(2, 1, 0)>;
+using JobsW5 = Jobs<job(1, 2, 1), job(1, 3, 1), job(0, 2, 2), job(2, 1, 1), job(2, 2, 0)>;
+using JobsW6 = Jobs<job(1, 2, 2), job(1, 3, 2), job(0, 3, 3), job(2, 2, 1), job(2, 3, 0)>;
+using JobsW7 = Jobs<job(0, 3, 2), job(1, 3, 3), job(2, 3, 1), kNone, kNone>;
+
+// O tiles owned by wavefront w (matching the lists above): count, and (token block, value block).
+__device__ __forceinline__ int o_count(int w) { return (w == 5 || w == 6) ? 2 : 1; }
+__device__ __forceinline__ void o_tile(int w, int t, int& cb, int& db) {
+  // w2: (0,0)  w3: (0,1)  w4: (1,0)  w5: (1,1),(2,0)  w6: (2,1),(3,0)  w7: (3,1)
+  const int idx = (w == 2) ? 0 : (w == 3) ? 1 : (w == 4) ? 2 : (w == 5) ? 3 + t : (w == 6) ? 5 + t : 7;
+  cb = idx >> 1;
+  db = idx & 1;
+}
+
+template <typename TOut>
+__global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int l = tid & 63;
+
+  const unsigned nblk = gridDim.x;
+  unsigned bid = blockIdx.x;
+  if (nblk % (8 * NT) == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
+  const int tile = bid % NT;
+  const int64_t bh = bid / NT;
+  const int c0 = tile * DVT;
+  const int64_t T = p.T;
+  const int64_t nchunks = (T + C - 1) / C;
+
+  f4 S[2];  // wavefront w: S^T tiles (d_k block w, d_v block db)
+  {
+    const int lr = l & 15, lg = l >> 4;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int dk = 16 * w + 4 * lg, dv = 16 * db + lr;
+      f4 x = {0.f, 0.f, 0.f, 0.f};
+      if (p.s0) x = *reinterpret_cast<const f4*>(p.s0 + (bh * D + c0 + dv) * D + dk);
+      S[db] = x;
+      *reinterpret_cast<h4*>(&sm.s[dv][dk]) = to_h4(x);
+    }
+  }
+
+  const Streams sr = make_streams(p, bh, tid >= 256);
+  Stage st;
+  if (nchunks > 0) stage_load(st, sr, 0, tid, c0);
+
+  TOut* O = static_cast<TOut*>(p.o);
+  const int t = tid & 255, g8 = t & 15, rq = t >> 4;
+  for (int64_t ci = 0; ci < nchunks; ++ci) {
+    const int64_t t0 = ci * C;
+    const int n = (int)(T - t0 < C ? T - t0 : C);
+    __syncthreads();  // the previous chunk is done with every buffer
+
+    // ---- stage 1: per-channel prefix of log alpha over each group of 4 tokens
+    float gl[4][8];
+    if (tid < 256) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a += bf_at(st.g[i], e);
+          gl[i][e] = a;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<f4*>(&sm.pf.tot[rq][8 * g8 + 4 * h]) = f4{gl[3][4 * h], gl[3][4 * h + 1], gl[3][4 * h + 2], gl[3][4 * h + 3]};
+    }
+    __syncthreads();
+
+    // ---- stage 2: add the sums of the earlier groups; publish G
+    if (tid < 256) {
+      float off[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int qg = 0; qg < rq; ++qg) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const f4 x = *reinterpret_cast<const f4*>(&sm.pf.tot[qg][8 * g8 + 4 * h]);
+          off[4 * h] += x[0]; off[4 * h + 1] += x[1]; off[4 * h + 2] += x[2]; off[4 * h + 3] += x[3];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gl[i][e] += off[e];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<f4*>(&sm.pf.G[4 * rq + i][8 * g8 + 4 * h]) =
+              f4{gl[i][4 * h], gl[i][4 * h + 1], gl[i][4 * h + 2], gl[i][4 * h + 3]};
+      }
+    }
+    __syncthreads();
+
+    // ---- stage 3: scaled operand tiles, tables, values, beta
+    {
+      const int R = rq >> 2;  // block of this thread's 4 tokens
+      const float* Gm = &sm.pf.G[16 * R + 7][8 * g8];
+      if (tid < 256) {
+        const float* Ge = &sm.pf.G[16 * R + 15][8 * g8];
+        const float* Gl = &sm.pf.G[C - 1][8 * g8];
+        h8 klh[4], kdh[4], krh[4], kth[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float k = bf_at(st.x[i], e);
+            const float el = __expf(gl[i][e] - Gm[e]);          // e^{G_r - G_m}
+            const float er = __expf(fminf(Ge[e] - gl[i][e], 0.f));  // e^{G_end - G_r} <= 1
+            klh[i][e] = (_Float16)(k * el);
+            kdh[i][e] = (_Float16)(k * __frcp_rn(el));
+            krh[i][e] = (_Float16)(k * er);
+            kth[i][e] = (_Float16)(k * er * __expf(fminf(Gl[e] - Ge[e], 0.f)));  // e^{G_63 - G_r}
+          }
+          const int row = 4 * rq + i;
+          *reinterpret_cast<h8*>(&sm.kl[row][8 * g8]) = klh[i];
+          *reinterpret_cast<h8*>(&sm.kd[row][8 * g8]) = kdh[i];
+          *reinterpret_cast<h8*>(&sm.kr[row][8 * g8]) = krh[i];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          h4 col;
+          col[0] = kth[0][e]; col[1] = kth[1][e]; col[2] = kth[2][e]; col[3] = kth[3][e];
+          *reinterpret_cast<h4*>(&sm.kt[8 * g8 + e][kt_col(8 * g8 + e, 4 * rq)]) = col;
+        }
+        *reinterpret_cast<h8*>(&sm.v[t >> 2][8 * (t & 3)]) = bf8_to_h8(st.v);
+        if (tid < C) sm.tb.beta[tid] = __uint_as_float(static_cast<uint32_t>(st.beta) << 16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float* Gr = &sm.pf.G[4 * rq + i][8 * g8];
+          h8 qh;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qh[e] = (_Float16)(bf_at(st.x[i], e) * __expf(Gr[e] - Gm[e]));
+          *reinterpret_cast<h8*>(&sm.ql[4 * rq + i][8 * g8]) = qh;
+        }
+        if (tid >= 384) {  // tables, one channel per thread
+          const int ch = tid - 384;
+#pragma unroll
+          for (int R2 = 0; R2 < 4; ++R2) {
+            const float gm = sm.pf.G[16 * R2 + 7][ch];
+            sm.tb.em[R2][ch] = __expf(gm);
+#pragma unroll
+            for (int J2 = 0; J2 < R2; ++J2) sm.tb.fm[R2][J2][ch] = __expf(fminf(gm - sm.pf.G[16 * J2 + 15][ch], 0.f));
+          }
+          sm.tb.gc[ch] = __expf(sm.pf.G[C - 1][ch]);
+        }
+      }
+    }
+    __syncthreads();
+    if (ci + 1 < nchunks) stage_load(st, sr, t0 + C, tid, c0);
+
+    // ---- phase 1: X (waves 0,1), A / P / inverses / O (waves 2..7)
+    l = opaque(l);
+    int lr = l & 15, lg = l >> 4;
+    if (w == 7) {  // zero the upper P blocks that the O += P U step reads: (0,1) and (2,3)
+      for (int e = l; e < 2 * 16 * 16; e += 64) {
+        const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+        sm.pr.p[32 * blk + rr][32 * blk + 16 + cc] = (_Float16)0.f;
+      }
+    }
+    f4 X[4], Oacc[2];
+    if (w < 2) {
+      const int db = w, dv = 16 * db + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[i] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const h8 sb = frag8(&sm.s[0][0], LQ, 16 * db, 32 * kk, l);
+        const int ch = 32 * kk + 8 * lg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          X[i] = mfma32(scale8(frag8(&sm.kl[0][0], LQ, 16 * i, 32 * kk, l), &sm.tb.em[i][ch]), sb, X[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * i + 4 * lg;
+        const f4 be = *reinterpret_cast<const f4*>(&sm.tb.beta[c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[i][e] = be[e] * ((float)sm.v[c + e][dv] - X[i][e]);
+      }
+    } else {
+      switch (w) {
+        case 2: produce<JobsW2>(sm, l, Oacc); break;
+        case 3: produce<JobsW3>(sm, l, Oacc); break;
+        case 4: produce<JobsW4>(sm, l, Oacc); break;
+        case 5: produce<JobsW5>(sm, l, Oacc); break;
+        case 6: produce<JobsW6>(sm, l, Oacc); break;
+        default: produce<JobsW7>(sm, l, Oacc); break;
+      }
+    }
+    __syncthreads();
+
+    // ---- phase 2: block forward substitution (waves 0,1)
+    l = opaque(l);
+    lr = l & 15, lg = l >> 4;
+    if (w < 2) {
+      const int dv = 16 * w + lr;
+      h4 an[6], tdf[4];
+#pragma unroll
+      for (int i = 0, m = 0; i < 4; ++i) {
+        tdf[i] = frag4(&sm.pr.td[i][0][0], LT, 0, 0, l);
+#pragma unroll
+        for (int j = 0; j < i; ++j, ++m) an[m] = frag4(&sm.pr.an[0][0], LC, 16 * i, 16 * j, l);
+      }
+      h4 Uh[4];
+#pragma unroll
+      for (int i = 0, m = 0; i < 4; ++i) {
+        f4 acc = X[i];
+#pragma unroll
+        for (int j = 0; j < i; ++j, ++m) acc = mfma16(an[m], Uh[j], acc);
+        Uh[i] = to_h4(mfma16(tdf[i], to_h4(acc), f4{0.f, 0.f, 0.f, 0.f}));
+        *reinterpret_cast<h4*>(&sm.pr.u[dv][16 * i + 4 * lg]) = Uh[i];
+      }
+    }
+    __syncthreads();
+
+    // ---- phase 3: O += U^T P^T, output (waves 2..7); S <- S Diag(Gamma_63) + U^T (K e^{G_63 - G})
+    l = opaque(l);
+    lr = l & 15, lg = l >> 4;
+    if (w >= 2) {
+      const int no = o_count(w);
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        if (t2 >= no) continue;
+        int cb, db;
+        o_tile(w, t2, cb, db);
+        f4 acc = Oacc[t2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          if (kc == 1 && cb < 2) continue;
+          acc = mfma32(frag8(&sm.pr.u[0][0], LC, 16 * db, 32 * kc, l), frag8(&sm.pr.p[0][0], LC, 16 * cb, 32 * kc, l), acc);
+        }
+        const int c = 16 * cb + lr;
+        if (c < n) store_o4<TOut>(O, (bh * T + t0 + c) * D + c0 + 16 * db + 4 * lg, acc);
+      }
+    }
+    {
+      const bool snap = p.s_ckpt && n == C && ((t0 + n) % p.ckpt_every) == 0;
+      const int dkr = 16 * w + lr;
+      const int dk = 16 * w + 4 * lg;
+      const f4 gcv = *reinterpret_cast<const f4*>(&sm.tb.gc[dk]);
+      h8 ka[2];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) ka[kc] = *reinterpret_cast<const h8*>(&sm.kt[dkr][kt_col(dkr, 32 * kc + 8 * lg)]);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        f4 acc = S[db] * gcv;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) acc = mfma32(ka[kc], frag8(&sm.pr.u[0][0], LC, 16 * db, 32 * kc, l), acc);
+        S[db] = acc;
+        const int dv = 16 * db + lr;
+        *reinterpret_cast<h4*>(&sm.s[dv][dk]) = to_h4(acc);
+        if (snap) {
+          const int64_t idx = (t0 + n) / p.ckpt_every - 1;
+          *reinterpret_cast<f4*>(p.s_ckpt + ((bh * p.n_ckpt + idx) * D + c0 + dv) * D + dk) = acc;
+        }
+      }
+    }
+  }
+
+  if (p.s_final) {
+    const int lr = l & 15, lg = l >> 4;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int dk = 16 * w + 4 * lg, dv = 16 * db + lr;
+      *reinterpret_cast<f4*>(p.s_final + (bh * D + c0 + dv) * D + dk) = S[db];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kda_mfma(const ChunkArgs& a, hipStream_t s) {
+  const int64_t blocks = a.B * a.H * NT;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (a.out_dtype == GDN_BF16)
+    hipLaunchKernelGGL((kda_chunk_mfma_kernel<__hip_bfloat16>), dim3((unsigned)blocks), dim3(NTH), 0, s, a);
+  else
+    hipLaunchKernelGGL((kda_chunk_mfma_kernel<float>), dim3((unsigned)blocks), dim3(NTH), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

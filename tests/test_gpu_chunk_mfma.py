@@ -135,3 +135,76 @@ def test_workload_long_prefill_snapshots_sampled_heads():
     ec = rel_l2(sc[:, heads], c_ref)
     print(f"long prefill rel-L2 o={eo:.3e} s_final={es:.3e} snapshots={ec:.3e}")
     assert eo <= TOL_BF16 and es <= TOL_BF16 and ec <= TOL_BF16
+
+
+# ------------------------------------------------------------------ KDA (per-channel decay)
+@pytest.mark.parametrize("T", [1, 64, 200, 1000])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_kda_mfma_small(T, out_dtype):
+    say(f"mfma kda T={T} out={out_dtype}")
+    inp = synth.make_prefill(1, 3, T, 128, 128, torch.bfloat16, kda=True, s0_std=0.01, seed=50 + T)
+    o, sf, _ = _gpu(True, inp, out_dtype=out_dtype)
+    o_ref, s_ref, _ = _ref(True, inp)
+    eo, es = rel_l2(o, o_ref), rel_l2(sf, s_ref)
+    print(f"kda rel-L2 o={eo:.3e} s_final={es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    if out_dtype == torch.float32:
+        assert eo <= 1e-3
+
+
+def test_kda_mfma_equal_channel_gates_match_gdn():
+    """KDA with the same rate on every key channel is the gated delta rule ("Attention,
+    Part 4", section 7): the two matrix-core kernels agree to within the bf16 tolerance."""
+    say("mfma kda == gdn for equal gates")
+    inp = synth.make_prefill(2, 2, 300, 128, 128, torch.bfloat16, s0_std=0.01, seed=61)
+    kinp = dict(inp)
+    kinp["log_alpha"] = inp["log_alpha"][..., None].expand(2, 2, 300, 128).contiguous()
+    o1, s1, _ = _gpu(False, inp, out_dtype=torch.float32)
+    o2, s2, _ = _gpu(True, kinp, out_dtype=torch.float32)
+    assert rel_l2(o2, o1) <= 1e-3 and rel_l2(s2, s1) <= 1e-3
+
+
+def test_kda_mfma_strong_gates():
+    """log alpha in [-1.2, -0.5] per channel: e^{-G} reaches e^{77} inside a 64-token chunk,
+    far beyond half precision; the per-block reference points keep every operand bounded."""
+    say("mfma kda strong gates")
+    inp = synth.make_prefill(1, 2, 256, 128, 128, torch.bfloat16, kda=True, s0_std=0.01, seed=62,
+                             log_alpha_range=(-1.2, -0.5))
+    o, sf, _ = _gpu(True, inp, out_dtype=torch.float32)
+    o_ref, s_ref, _ = _ref(True, inp)
+    assert torch.isfinite(o).all() and torch.isfinite(sf).all()
+    assert rel_l2(o, o_ref) <= TOL_BF16 and rel_l2(sf, s_ref) <= TOL_BF16
+
+
+def test_kda_mfma_snapshots_resume_empty():
+    import gated_deltanet_state_amd as g
+    say("mfma kda snapshots/resume/empty")
+    T, every = 448, 128
+    inp = synth.make_prefill(1, 2, T, 128, 128, torch.bfloat16, kda=True, s0_std=0.01, seed=63)
+    o, sf, sc = _gpu(True, inp, ckpt_every=every, out_dtype=torch.float32)
+    o_ref, s_ref, c_ref = _ref(True, inp, ckpt_every=every)
+    assert sc.shape == (1, 2, 3, 128, 128) and rel_l2(sc, c_ref) <= TOL_BF16
+    tail = {k: (v[:, :, 256:].contiguous() if k != "s0" else None) for k, v in inp.items()}
+    tail["s0"] = sc[:, :, 1].cpu()
+    o2, sf2, _ = _gpu(True, tail, out_dtype=torch.float32)
+    assert torch.equal(o2, o[:, :, 256:]) and torch.equal(sf2, sf)
+    e = synth.make_prefill(1, 2, 0, 128, 128, torch.bfloat16, kda=True, s0_std=0.01, seed=64)
+    o, sf, _ = _gpu(True, e)
+    assert o.shape == (1, 2, 0, 128) and torch.equal(sf.cpu(), e["s0"])
+
+
+def test_workload_kda_full_size_sampled_heads():
+    """B=2, H=32, T=8192, d=128, chunk 64, bf16, per-channel gates: the oracle follows 3
+    sampled (batch, head) streams through the whole sequence."""
+    say("kda workload B=2 H=32 T=8192")
+    inp = synth.make_workload(4)
+    o, sf, _ = _gpu(True, inp)
+    sel = [(0, 0), (0, 17), (1, 31)]
+    sub = {k: (torch.stack([v[b, h] for b, h in sel])[None].contiguous() if v is not None else None)
+           for k, v in inp.items()}
+    o_ref, s_ref, _ = _ref(True, sub)
+    og = torch.stack([o[b, h] for b, h in sel])[None]
+    sg = torch.stack([sf[b, h] for b, h in sel])[None]
+    eo, es = rel_l2(og, o_ref), rel_l2(sg, s_ref)
+    print(f"kda workload rel-L2 o={eo:.3e} s_final={es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16
