@@ -14,9 +14,12 @@
 // against 7 D^2 flops.  Layout of the work: a group of 2D lanes owns one state; lane
 // (row group rg, column quad c4) holds rows rg, rg+8, ... of columns 4c4..4c4+3 as float4,
 // so each wavefront load/store instruction moves whole contiguous rows (coalesced 16-byte
-// accesses).  The two row dot products are reduced across the D/4 lanes of a row with
-// cross-lane shuffles; all loads of the state are issued before any reduction so that the
-// whole 64 KiB state of a workgroup is in flight at once.
+// accesses).  The 2 x (D/8) row dot products of a lane are reduced across the D/4 lanes of
+// its row group by one butterfly reduce-scatter (D/4 - 1 exchanges, DPP and ds_swizzle, no
+// LDS memory traffic) that leaves one finished dot product per lane; the per-row corrections
+// are then broadcast back through a small LDS line private to the wavefront.  All loads of
+// the state are issued before any reduction, so the whole 64 KiB state of a workgroup is in
+// flight at once.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
@@ -36,15 +39,52 @@ __device__ __forceinline__ void st_out(__hip_bfloat16* p, int64_t i, float x) {
   p[i] = __float2bfloat16(x);  // round to nearest even
 }
 
-// Sum over aligned groups of W lanes (W a power of two <= 64).
+// Exchange with lane ^ M inside aligned groups of 32 lanes: DPP quad permutes for M = 1, 2
+// (no LDS traffic), ds_swizzle bit-mask mode otherwise.
+template <int M>
+__device__ __forceinline__ float xor_lane(float x) {
+  const int v = __float_as_int(x);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, false));  // [1,0,3,2]
+  else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, false));  // [2,3,0,1]
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(v, (M << 10) | 0x1f));
+}
+
+// Sum over aligned groups of W lanes (W a power of two <= 32); every lane gets the sum.
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int m = W / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, W);
+  if constexpr (W >= 32) x += xor_lane<16>(x);
+  if constexpr (W >= 16) x += xor_lane<8>(x);
+  if constexpr (W >= 8) x += xor_lane<4>(x);
+  if constexpr (W >= 4) x += xor_lane<2>(x);
+  if constexpr (W >= 2) x += xor_lane<1>(x);
   return x;
 }
 
+// Butterfly reduce-scatter of N values over aligned groups of N lanes: on return vals[0] of
+// lane j (j = lane mod N) holds the group sum of value j.  At the step with partner lane ^ M
+// each lane keeps the half of its 2M values selected by its bit M and receives the other half
+// from its partner: N - 1 exchanges in all instead of N log2 N for N separate reductions.
+template <int M>
+__device__ __forceinline__ void scatter_step(float* vals, int lane) {
+  const bool upper = (lane & M) != 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const float send = upper ? vals[i] : vals[M + i];
+    const float keep = upper ? vals[M + i] : vals[i];
+    vals[i] = keep + xor_lane<M>(send);
+  }
+}
+template <int N>
+__device__ __forceinline__ void reduce_scatter(float* vals, int lane) {
+  if constexpr (N >= 32) scatter_step<16>(vals, lane);
+  if constexpr (N >= 16) scatter_step<8>(vals, lane);
+  if constexpr (N >= 8) scatter_step<4>(vals, lane);
+  if constexpr (N >= 4) scatter_step<2>(vals, lane);
+  if constexpr (N >= 2) scatter_step<1>(vals, lane);
+}
+
 constexpr int kThreads = 256;
+typedef float f4v __attribute__((ext_vector_type(4)));
 
 template <int D, typename TIn, typename TOut>
 __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ state,
@@ -58,21 +98,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ st
   constexpr int RG = 8;                   // row groups per state
   constexpr int TPS = LPR * RG;           // lanes per state = 2D
   constexpr int SPB = kThreads / TPS;     // states per workgroup
-  constexpr int RPT = D / RG;             // rows per lane
-  static_assert(D % 32 == 0 || D == 16, "D must be 16, 32, 64 or 128");
-  static_assert(SPB >= 1 && kThreads % TPS == 0, "bad decode tiling");
+  constexpr int RPT = D / RG;             // rows per lane; 2 RPT == LPR partial sums to reduce
+  static_assert(D == 16 || D == 32 || D == 64 || D == 128, "D must be 16, 32, 64 or 128");
+  static_assert(2 * RPT == LPR, "one reduced value per lane");
+  __shared__ float ush[SPB][D];           // per-row corrections, broadcast inside a lane group
 
   const int tid = threadIdx.x;
-  const int64_t s = static_cast<int64_t>(blockIdx.x) * SPB + tid / TPS;
+  const int slot = tid / TPS;
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * SPB + slot;
   if (s >= n_states) return;  // whole lane groups drop out together
   const int lt = tid % TPS;
-  const int c4 = lt % LPR;
+  const int c4 = lt % LPR;                // column quad, and the lane's index inside its row group
   const int rg = lt / LPR;
 
-  float4* S = reinterpret_cast<float4*>(state + s * D * D);
-  float4 st[RPT];
+  // the states stream through once per step: non-temporal loads and stores keep them from
+  // displacing the small per-token inputs in the caches
+  f4v* S = reinterpret_cast<f4v*>(state + s * D * D);
+  f4v st[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) st[i] = S[(rg + RG * i) * LPR + c4];
+  for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(&S[(rg + RG * i) * LPR + c4]);
 
   float kk[4], qq[4];
 #pragma unroll
@@ -83,31 +127,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ st
   const float b = ld_in(beta, s);
   const float a = __expf(ld_in(log_alpha, s));
 
-  float r[RPT], p[RPT];
+  // partial dot products: value 2i = s_row(i) . k, value 2i + 1 = s_row(i) . q
+  float vals[2 * RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    r[i] = st[i].x * kk[0] + st[i].y * kk[1] + st[i].z * kk[2] + st[i].w * kk[3];
-    p[i] = st[i].x * qq[0] + st[i].y * qq[1] + st[i].z * qq[2] + st[i].w * qq[3];
+    vals[2 * i] = st[i][0] * kk[0] + st[i][1] * kk[1] + st[i][2] * kk[2] + st[i][3] * kk[3];
+    vals[2 * i + 1] = st[i][0] * qq[0] + st[i][1] * qq[1] + st[i][2] * qq[2] + st[i][3] * qq[3];
   }
-  float kq = kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3];
-  kq = group_sum<LPR>(kq);
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    r[i] = group_sum<LPR>(r[i]);
-    p[i] = group_sum<LPR>(p[i]);
-  }
+  const float kq = group_sum<LPR>(kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3]);
+  reduce_scatter<LPR>(vals, c4);
+
+  // lane c4 of the group now holds r (c4 even) or p (c4 odd) of row rg + RG * (c4 / 2)
+  const int row = rg + RG * (c4 >> 1);
+  const float r_or_p = vals[0];
+  const float u = b * (ld_in(v, s * D + row) - a * r_or_p);        // meaningful on even lanes
+  const float u_even = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(u), 0xA0, 0xf, 0xf, false));  // [0,0,2,2]
+  if (c4 & 1) st_out(o, s * D + row, a * r_or_p + u_even * kq);
+  else ush[slot][row] = u;
+  // the rows of this lane group were written by lanes of the same wavefront
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int row = rg + RG * i;
-    const float u = b * (ld_in(v, s * D + row) - a * r[i]);
-    float4 x = st[i];
-    x.x = a * x.x + u * kk[0];
-    x.y = a * x.y + u * kk[1];
-    x.z = a * x.z + u * kk[2];
-    x.w = a * x.w + u * kk[3];
-    S[row * LPR + c4] = x;
-    if (c4 == 0) st_out(o, s * D + row, a * p[i] + u * kq);
+    const float ui = ush[slot][rg + RG * i];
+    f4v x = st[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = a * x[j] + ui * kk[j];
+    __builtin_nontemporal_store(x, &S[(rg + RG * i) * LPR + c4]);
   }
 }
 
