@@ -52,7 +52,7 @@ def _src_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel: str, src_files, per_launch_fallback=None):
+def _traffic(kernel: str, src_files):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
     current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
@@ -81,22 +81,25 @@ def time_launches(fn, steps: int, warmup: int, torch) -> float:
     return s.elapsed_time(e) / steps
 
 
-def cpu_baseline_prefill(inp, n_streams: int, H: int):
-    """fp64 oracle on `n_streams` whole (batch, head) streams of the workload, all host cores."""
+def cpu_baseline_prefill(inp, min_seconds: float = 10.0, max_reps: int = 200):
+    """The fp64 oracle, as it stands, on the whole workload (every (batch, head) stream, all
+    tokens) on all host cores, repeated until at least `min_seconds` of wall time."""
     import oracle
     oracle.build(force=False)
-    B, Hh, T, d = inp["q"].shape
-    sel = [(i // Hh, i % Hh) for i in range(n_streams)]
-    sub = {k: (inp[k][[b for b, _ in sel], [h for _, h in sel]].unsqueeze(0).contiguous()
-               if inp[k] is not None else None) for k in inp}
+    B, H, T, d = inp["q"].shape
+    args = (inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], inp["s0"])
+    reps, threads = 0, 0
     t0 = time.perf_counter()
-    _, _, _, threads = oracle.forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["log_alpha"], sub["s0"],
-                                      return_threads=True)
-    dt = time.perf_counter() - t0
-    tokens = n_streams * T / H  # a token carries all H heads
+    while True:
+        _, _, _, threads = oracle.forward(*args, return_threads=True)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            break
+    tokens = reps * B * T  # a token carries all H heads
     return {"value": round(tokens / dt / 1e6, 6), "unit": "Mtok/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_streams} of {B * Hh} (batch, head) streams, all {T} tokens each, fp64 token loop; "
-                      f"{dt:.2f} s wall; throughput scaled to tokens of {H} heads"}
+            "sample": f"whole workload ({B * H} streams x {T} tokens) repeated {reps} times, fp64 token "
+                      f"loop, {dt:.1f} s wall"}
 
 
 def main():
@@ -105,9 +108,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "kda", "all"], default="all",
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "kda", "copy", "all"], default="all",
                     help="run a subset (for profiling); the JSON line needs 'all' or 'prefill'")
-    ap.add_argument("--cpu-streams", type=int, default=0, help="oracle sample size (0 = host cores)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -150,7 +152,7 @@ def main():
         nbytes = prefill_bytes(c.B, c.H, c.T, c.Dk)
         gbs = nbytes / (ms * 1e-3) / 1e9
         tflops = flops / (ms * 1e-3) / 1e12
-        traffic = _traffic("gdn_chunk_mfma", ["gdn_chunk_mfma.hip"])
+        traffic = _traffic("gdn_chunk_mfma", ["gdn_chunk_mfma.hip", "gdn_mfma_common.h"])
         out.update({
             "metric": METRIC, "value": round(mtoks, 3), "unit": "Mtok/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -167,11 +169,8 @@ def main():
         })
         log(f"prefill: {ms*1e3:.1f} us/step, {mtoks:.1f} Mtok/s, {gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
         if not args.no_cpu_baseline:
-            import oracle
-            oracle.build(force=False)
-            n = args.cpu_streams or min(c.B * c.H, oracle.hardware_threads())
-            log(f"cpu baseline: oracle on {n} streams")
-            out["cpu_baseline"] = cpu_baseline_prefill(sets[0], n, c.H)
+            log("cpu baseline: fp64 oracle on the host cores")
+            out["cpu_baseline"] = cpu_baseline_prefill(sets[0])
         del dsets, outs, sets
         torch.cuda.empty_cache()
 
@@ -260,12 +259,26 @@ def main():
         ms = time_launches(kstep, 3, 1, torch)
         nb = prefill_bytes(c.B, c.H, c.T, c.Dk, kda=True)
         fl = c.B * c.H * c.T * prefill_flops_per_head_token(c.chunk, c.Dk)
+        gb = nb / (ms * 1e-3) / 1e9
         extra["kda_prefill"] = {
             "workload": c.name, "B": c.B, "H": c.H, "T": c.T, "ms": round(ms, 4),
             "Mtok_per_s": round(c.B * c.T / (ms * 1e-3) / 1e6, 3),
-            "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gb, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gb / HBM_PEAK_GBS, 4),
+                         "traffic": _traffic("kda_chunk_mfma", ["kda_chunk_mfma.hip", "gdn_mfma_common.h"]),
+                         "kernel": "kda_chunk_mfma_kernel", "algorithmic_bytes": nb},
             "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         log(f"kda prefill: {ms:.3f} ms")
+
+    # ---------------- plain device copy of known size: calibrates the HBM byte counters ----------------
+    if args.only == "copy":
+        n = 1 << 28  # 1 GiB of fp32
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        ms = time_launches(lambda i: dst.copy_(src), 5, 1, torch)
+        extra["copy"] = {"bytes_read": 4 * n, "bytes_written": 4 * n, "ms": round(ms, 4),
+                         "GBps": round(8 * n / (ms * 1e-3) / 1e9, 1)}
+        log(f"copy: {ms:.3f} ms, {8 * n / (ms * 1e-3) / 1e9:.0f} GB/s (read + write)")
 
     if "metric" not in out:
         print(json.dumps(extra))
