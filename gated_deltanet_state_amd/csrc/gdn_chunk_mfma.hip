@@ -8,26 +8,27 @@
 // d_v x d_k convention, for a chunk of tokens r = 0..63 entering with state S, with
 // G_r = sum_{s<=r} log alpha_s, gamma_r = e^{G_r} and D_rj = e^{G_r - G_j}:
 //   A = strict_tril(diag(beta) (K K^T * D))           (64 x 64)
+//   T = (I + A)^{-1}                                   unit lower triangular
 //   X = diag(beta) (V - diag(gamma) K S^T)             (64 x d_v)
-//   (I + A) U = X                                      unit lower-triangular system
+//   U = T X
 //   O = diag(gamma) Q S^T + tril(Q K^T * D) U          outputs
 //   S <- gamma_63 S + U^T diag(e^{G_63 - G}) K         state handed to the next chunk
 //
 // Work decomposition: a workgroup owns one (batch, head) stream and a 32-row slice of the
 // value channels (the recurrence multiplies S only from the right, so value rows evolve
 // independently); the four slices of a stream are placed on the same XCD so they share its
-// L2.  The slice of S lives in MFMA accumulators (fp32) for the whole sequence.
-//
-// Eight wavefronts run a two-stage pipeline over the chunks.  Everything that does not
-// depend on the state -- the decay-weighted Gram matrix A, the causal scores P and the
-// inverses of the 16x16 diagonal blocks of (I + A) -- is produced for chunk c+1 by six
-// wavefronts while two wavefronts run chunk c's state-coupled triangular substitution, so
-// the latency-bound parts of the two stages overlap.  Per chunk:
-//   A: X = ... K S^T (waves 0,1) and O = diag(gamma) Q S^T (waves 2..5)   [chunk c]
-//   S: stage chunk c+1 (fp16 tiles, transposed keys, gate tables); prefetch chunk c+2
-//   B: U_i = T_ii (X_i - sum_{j<i} A_ij U_j) (waves 0,1)                   [chunk c]
-//      A, P, T_ii of chunk c+1 (waves 2..7)
-//   C: O += P U, write o (waves 2..5); S <- gamma S + U^T diag(.) K (all)  [chunk c]
+// L2.  Eight wavefronts take fixed roles (waves w and w + 4 share a SIMD):
+//   0, 1  state chain: each keeps a 16 x 128 block of S in fp32 MFMA accumulators for the
+//         whole sequence and runs X, U = T X and the state update with every operand
+//         regrouped in registers (no LDS round trip on the chunk-to-chunk dependency);
+//   4, 5  outputs of two 16-token blocks each: O = diag(gamma) Q S^T + P U;
+//   6, 7  one chunk ahead: the diagonal 16x16 blocks of A, their inverses and the
+//         off-diagonal blocks of T (wave 6); the off-diagonal blocks of A (wave 7); the
+//         causal scores P = tril(Q K^T * D) (both);
+//   2, 3  staging: keys (row-major, and transposed for the state update), queries, values
+//         and the gate tables, converted to fp16 and written to LDS one or two chunks ahead.
+// Each iteration has two barrier-separated phases; iteration c works on chunk c (chain,
+// outputs), chunk c + 1 (producers) and chunks c + 1, c + 2 (staging).
 // The products run on v_mfma_f32_16x16x32_f16 / 16x16x16_f16 with fp32 accumulation.
 // bf16 inputs convert exactly to fp16 (|x| <= 65504); derived operands (S, P, U, T) are
 // rounded to fp16, whose 11-bit significand keeps the bf16-output error budget.
@@ -50,221 +51,547 @@ constexpr int C = 64;        // chunk length
 constexpr int DVT = 32;      // value rows per workgroup
 constexpr int NT = D / DVT;  // workgroups per stream
 constexpr int NTH = 512;     // threads per workgroup (8 wavefronts)
-constexpr int LQ = D + 8;    // row stride (halves) of [token][channel] tiles
+constexpr int LQ = D + 16;   // row stride (halves) of [token][channel] tiles: 288 bytes = 72 banks
 constexpr int LC = C + 8;    // row stride (halves) of [channel][token] and [token][token] tiles
 constexpr int LT = 24;       // row stride (halves) of 16x16 blocks
 
-// Per-chunk gate tables (double-buffered with the chunk's other state-independent data).
+// Per-chunk gate tables.
 struct alignas(16) Gates {
   alignas(16) float G[C];     // inclusive prefix of log alpha
   alignas(16) float gam[C];   // e^{G_r}
   alignas(16) float dec[C];   // e^{G_63 - G_r}
   alignas(16) float beta[C];
   alignas(16) float el[C];    // e^{G_r - G_ref(block of r)}, G_ref(R) = G_{16R-1} (0 for R = 0)
-  alignas(16) float er[4][C]; // er[R][j] = e^{G_ref(R) - G_j} for j < 16 R
+  alignas(16) float nbel[C];  // -beta_r el_r
+  alignas(16) float er[3][C]; // er[R-1][j] = e^{G_ref(R) - G_j} for j < 16 R, R = 1..3
 };
 
+// Buffers hold data of one chunk: keys and gate tables by chunk mod 3, the others by chunk
+// mod 2.  Bank
+// layout (gfx950 LDS: 16-byte accesses are served 32 lanes at a time over 128 four-byte banks):
+// a 16-row x 32-column fragment read is conflict-free when the row stride is an odd multiple
+// of 8 banks, hence the 288-byte rows of the [token][channel] tiles.
 struct alignas(16) Smem {
-  alignas(16) _Float16 q[C][LQ];           // queries of the staged chunk        [token][d_k]
-  alignas(16) _Float16 k[C][LQ];           // keys of the staged chunk           [token][d_k]
-  alignas(16) _Float16 kt[2][D][LC];       // keys transposed (swizzled)         [d_k][token]
-  alignas(16) _Float16 s[DVT][LQ];         // fp16 copy of the state slice       [d_v][d_k]
-  alignas(16) _Float16 p[2][C][LC];        // tril(Q K^T * D), inclusive          [token][token]
-  alignas(16) _Float16 an[2][C][LC];       // -A, off-diagonal 16x16 blocks       [token][token]
-  alignas(16) _Float16 td[2][4][16][LT];   // inverses of the diagonal blocks of (I + A), row-major
-  alignas(16) _Float16 nt[4][16][LT];      // scratch: transposed diagonal blocks of A
-  alignas(16) _Float16 u[DVT][LC];         // U                                   [d_v][token]
-  alignas(16) _Float16 ud[DVT][LC];        // diag(e^{G_63 - G}) U                [d_v][token]
-  alignas(16) _Float16 v[C][DVT + 8];      // value slice of the staged chunk     [token][d_v]
-  alignas(16) Gates gt[2];
+  alignas(16) _Float16 k[3][C][LQ];      // keys                                  [token][d_k]
+  alignas(16) _Float16 q[2][C][LQ];      // queries                               [token][d_k]
+  alignas(16) _Float16 s[DVT][LQ];       // fp16 state slice entering the chain's chunk [d_v][d_k]
+  alignas(16) uint16_t vt[2][DVT][LC];   // value slice, bf16 bits                [d_v][token]
+  alignas(16) _Float16 t[2][C][LC];      // T = (I + A)^{-1}, upper blocks zero; A_JJ staged on the diagonal
+  alignas(16) _Float16 p[2][C][LC];      // tril(Q K^T * D), upper blocks zero     [token][token]
+  alignas(16) _Float16 an[6][16][LT];    // -A, off-diagonal blocks (R, J), R > J
+  alignas(16) _Float16 u[DVT][LC];       // U of the chain's chunk                [d_v][token]
+  alignas(16) Gates gt[3];
 };
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+__device__ __forceinline__ int kbuf(int64_t chunk) { return (int)(((chunk % 3) + 3) % 3); }
 
-// ------------------------------------------------------------------------------------------
-// Staging.  Global -> registers through buffer loads on per-stream buffer descriptors: the
-// hardware range check returns zeros for tokens at or past the end of the stream, which pads
-// a ragged last chunk with identity steps (k = v = q = 0, beta = 0, log alpha = 0) without
-// branches, and buffer loads never touch the LDS counter, so waits on LDS traffic never wait
-// for the prefetch.  Threads 0..255 stage keys (and values, gates), threads 256..511 queries.
+constexpr int an_idx(int R, int J) { return R * (R - 1) / 2 + J; }
 
-struct Streams {
-  __amdgpu_buffer_rsrc_t qk, v, beta, g;
-};
-
-__device__ __forceinline__ Streams make_streams(const ChunkArgs& p, int64_t bh, bool is_q) {
-  const int64_t tok = bh * p.T;
-  const int bytes_qkv = (int)(p.T * D * 2);
-  const int bytes_tok = (int)(p.T * 2);
-  const void* qk = is_q ? p.q : p.k;
-  Streams s;
-  s.qk = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)qk + tok * D), 0, bytes_qkv, kRsrcWord3);
-  s.v = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.v + tok * D), 0, bytes_qkv, kRsrcWord3);
-  s.beta = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.beta + tok), 0, bytes_tok, kRsrcWord3);
-  s.g = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.log_alpha + tok), 0, bytes_tok, kRsrcWord3);
-  return s;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void* base, int64_t elem0, int64_t n_elems) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)base + elem0), 0, (int)(n_elems * 2), kRsrcWord3);
 }
-
-struct Stage {
-  v4u x[4];                // rows 4*(t/16)+i, channels 8*(t%16)..+7 (t = tid mod 256)
-  v4u v;                   // key threads: row t/4, value channels c0 + 8*(t%4)..+7
-  unsigned short beta, g;  // wavefront 0: token tid
-};
-
-__device__ __forceinline__ void stage_load(Stage& st, const Streams& sr, int64_t t0, int tid, int c0) {
-  const int t = tid & 255;
-  const int g8 = t & 15, rq = t >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    st.x[i] = __builtin_amdgcn_raw_buffer_load_b128(sr.qk, (int)(((t0 + 4 * rq + i) * D + 8 * g8) * 2), 0, 0);
-  if (tid < 256)
-    st.v = __builtin_amdgcn_raw_buffer_load_b128(sr.v, (int)(((t0 + (t >> 2)) * D + c0 + 8 * (t & 3)) * 2), 0, 0);
-  if (tid < C) {
-    st.beta = __builtin_amdgcn_raw_buffer_load_b16(sr.beta, (int)((t0 + tid) * 2), 0, 0);
-    st.g = __builtin_amdgcn_raw_buffer_load_b16(sr.g, (int)((t0 + tid) * 2), 0, 0);
-  }
+__device__ __forceinline__ v4u ld_b128(__amdgpu_buffer_rsrc_t r, int64_t elem) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)(elem * 2), 0, 0);
 }
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ h8 lds8(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
+__device__ __forceinline__ h4 lds4(const _Float16* p) { return *reinterpret_cast<const h4*>(p); }
 
-// Register -> LDS: fp16 tiles (row-major keys and queries, transposed keys into buffer b)
-// and the gate tables of buffer b.
-__device__ __forceinline__ void stage_store(const Stage& st, Smem& sm, int b, int tid) {
-  const int t = tid & 255;
-  const int g8 = t & 15, rq = t >> 4;
-  if (tid >= 256) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<h8*>(&sm.q[4 * rq + i][8 * g8]) = bf8_to_h8(st.x[i]);
-    return;
-  }
-  h8 kh[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    kh[i] = bf8_to_h8(st.x[i]);
-    *reinterpret_cast<h8*>(&sm.k[4 * rq + i][8 * g8]) = kh[i];
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h4 col;
-    col[0] = kh[0][e]; col[1] = kh[1][e]; col[2] = kh[2][e]; col[3] = kh[3][e];
-    *reinterpret_cast<h4*>(&sm.kt[b][8 * g8 + e][kt_col(8 * g8 + e, 4 * rq)]) = col;
-  }
-  *reinterpret_cast<h8*>(&sm.v[t >> 2][8 * (t & 3)]) = bf8_to_h8(st.v);
-  if (tid < C) {
-    const float x = wave_prefix_sum(__uint_as_float(static_cast<uint32_t>(st.g) << 16));
-    const float glast = __shfl(x, C - 1, 64);
-    const float gr1 = __shfl(x, 15, 64), gr2 = __shfl(x, 31, 64), gr3 = __shfl(x, 47, 64);
-    const int R = tid >> 4;
-    const float gref = R == 0 ? 0.f : (R == 1 ? gr1 : (R == 2 ? gr2 : gr3));
-    Gates& g = sm.gt[b];
-    g.G[tid] = x;
-    g.gam[tid] = __expf(x);
-    g.dec[tid] = __expf(glast - x);
-    g.beta[tid] = __uint_as_float(static_cast<uint32_t>(st.beta) << 16);
-    g.el[tid] = __expf(x - gref);
-    g.er[1][tid] = __expf(fminf(gr1 - x, 0.f));
-    g.er[2][tid] = __expf(fminf(gr2 - x, 0.f));
-    g.er[3][tid] = __expf(fminf(gr3 - x, 0.f));
-  }
+// Dword m of the 16-bit transpose: halves e of dwords x (low result half) and y (high).
+__device__ __forceinline__ uint32_t pick2(uint32_t x, uint32_t y, int e) {
+  return __builtin_amdgcn_perm(y, x, (e & 1) ? 0x07060302u : 0x05040100u);
 }
 
 // ------------------------------------------------------------------------------------------
-// State-independent products of one chunk (buffer b).  A Gram job is a 16x16 tile (R, J) of A
-// (kind 0, from K K^T) or of P (kind 1, from Q K^T), computed as (M = j, N = r) so the lane
-// holds a row of the tile: r = 16 R + lr, j = 16 J + 4 lg + i.
-template <int KIND>
-__device__ __forceinline__ f4 gram_scale(const Gates& g, int R, int J, int lr, int lg, f4 acc) {
-  const int r = 16 * R + lr, j0 = 16 * J + 4 * lg;
+// Decay-weighted Gram tiles.  A tile (R, J) of A (from K K^T) or of P (from Q K^T) is computed
+// as (M = j, N = r), so the lane holds a row of the tile: r = 16 R + lr, j = 16 J + 4 lg + e.
+// Off the diagonal the decay splits at the reference point (both factors <= 1); on the
+// diagonal the factor e^{G_r - G_j} (j <= r) is formed directly and shared by A and P.
+__device__ __forceinline__ f4 offdiag_neg_a(const Gates& g, int R, int J, int lr, int lg, f4 acc) {
+  const int r = 16 * R + lr;
+  return (g.nbel[r] * *reinterpret_cast<const f4*>(&g.er[R - 1][16 * J + 4 * lg])) * acc;
+}
+__device__ __forceinline__ f4 offdiag_p(const Gates& g, int R, int J, int lr, int lg, f4 acc) {
+  const int r = 16 * R + lr;
+  return (g.el[r] * *reinterpret_cast<const f4*>(&g.er[R - 1][16 * J + 4 * lg])) * acc;
+}
+// e^{G_r - G_j} for r = 16 J + lr, j = 16 J + 4 lg + e, zero for j > r.
+__device__ __forceinline__ f4 diag_decay(const Gates& g, int J, int lr, int lg) {
+  const int r = 16 * J + lr, j0 = 16 * J + 4 * lg;
+  const float gr = g.G[r];
+  const f4 gj = *reinterpret_cast<const f4*>(&g.G[j0]);
   f4 f;
-  if (R == J) {
-    const float gr = g.G[r];
-    const f4 gj = *reinterpret_cast<const f4*>(&g.G[j0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = j0 + i;
-      const bool keep = KIND ? (j <= r) : (j < r);
-      const float e = __expf(fminf(gr - gj[i], 0.f));  // <= 1; masked entries are dropped below
-      f[i] = keep ? e : 0.f;
-    }
-  } else {
-    f = g.el[r] * *reinterpret_cast<const f4*>(&g.er[R][j0]);
-  }
-  return KIND == 0 ? (g.beta[r] * f) * acc : f * acc;
+  for (int e = 0; e < 4; ++e) f[e] = (j0 + e <= r) ? __expf(gr - gj[e]) : 0.f;
+  return f;
 }
 
-// Inverse of the unit lower-triangular diagonal block (I + N), N = A_JJ strictly lower, as
-// (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0) on 16x16x16 MFMAs.  With row(M) (lane holds
-// M[lr][4lg..+3], the A-operand layout) and col(M) (lane holds M[4lg..+3][lr], the B-operand
-// and accumulator layout): col(XY) = mfma(row X, col Y) and row(XY) = mfma(col Y, row X).
-// rowN arrives in registers; colN goes through an LDS transpose private to this wavefront.
-__device__ __forceinline__ void invert_diag(Smem& sm, int b, int J, f4 rowN, int lr, int lg) {
+// Inverses of the four unit lower-triangular diagonal blocks (I + N_J), N_J = A_JJ strictly
+// lower, as (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0) on 16x16x16 MFMAs.  With row(M)
+// (lane holds M[lr][4lg..+3], the A-operand layout) and col(M) (lane holds M[4lg..+3][lr], the
+// B-operand and accumulator layout): col(XY) = mfma(row X, col Y) and row(XY) = mfma(col Y,
+// row X); in particular col(N) = mfma(row N, col I).  Returns each inverse in both layouts
+// (the factors commute, so either order is the product).  The four chains are independent
+// and advance level by level so their MFMA latencies overlap.
+__device__ __forceinline__ void invert_diag4(const f4 (&rowN)[4], int lr, int lg, h4 (&Tr)[4], h4 (&Tc)[4]) {
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
   f4 eye;  // identity in either layout: element i of lane (lr, lg) is on the diagonal iff 4 lg + i == lr
 #pragma unroll
   for (int i = 0; i < 4; ++i) eye[i] = (4 * lg + i == lr) ? 1.f : 0.f;
-  const h4 rN = to_h4(rowN);
+  const h4 eyeh = to_h4(eye);
+  h4 rN[4], cN[4], n2ch[4], n2rh[4], n4ch[4], n4rh[4], p1[4], n8e[4], p2r[4];
+  f4 n2c[4], n4c[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sm.nt[J][4 * lg + i][lr] = rN[i];
-  // the transpose is written and read by this wavefront only: order the LDS accesses
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const h4 cN = *reinterpret_cast<const h4*>(&sm.nt[J][lr][4 * lg]);
-  const f4 n2c = mfma16(rN, cN, zero), n2r = mfma16(cN, rN, zero);
-  const h4 n2ch = to_h4(n2c), n2rh = to_h4(n2r);
-  const f4 n4c = mfma16(n2rh, n2ch, zero), n4r = mfma16(n2ch, n2rh, zero);
-  const f4 n8c = mfma16(to_h4(n4r), to_h4(n4c), zero);
-  const f4 p1r = mfma16(to_h4(n2c + eye), to_h4(eye - rowN), zero);
-  const f4 p2r = mfma16(to_h4(n4c + eye), to_h4(p1r), zero);
-  const f4 tr = mfma16(to_h4(n8c + eye), to_h4(p2r), zero);
-  *reinterpret_cast<h4*>(&sm.td[b][J][lr][4 * lg]) = to_h4(tr);
+  for (int J = 0; J < 4; ++J) rN[J] = to_h4(rowN[J]);
+#pragma unroll
+  for (int J = 0; J < 4; ++J) cN[J] = to_h4(mfma16(rN[J], eyeh, zero));
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    n2c[J] = mfma16(rN[J], cN[J], zero);
+    n2rh[J] = to_h4(mfma16(cN[J], rN[J], zero));
+  }
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    n2ch[J] = to_h4(n2c[J]);
+    n4c[J] = mfma16(n2rh[J], n2ch[J], zero);
+    n4rh[J] = to_h4(mfma16(n2ch[J], n2rh[J], zero));
+    p1[J] = to_h4(mfma16(to_h4(n2c[J] + eye), to_h4(eye - rowN[J]), zero));   // row((I - N)(I + N^2))
+  }
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    n4ch[J] = to_h4(n4c[J]);
+    n8e[J] = to_h4(mfma16(n4rh[J], n4ch[J], zero) + eye);                     // col(I + N^8)
+    p2r[J] = to_h4(mfma16(to_h4(n4c[J] + eye), p1[J], zero));                 // row(P1 (I + N^4))
+  }
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    Tr[J] = to_h4(mfma16(n8e[J], p2r[J], zero));                              // row(P2 (I + N^8))
+    Tc[J] = to_h4(mfma16(p2r[J], n8e[J], zero));                              // col(P2 (I + N^8))
+  }
 }
 
-// Job codes: kind << 4 | R << 2 | J.  Each producing wavefront takes up to four jobs; jobs of
-// one column J reuse the key fragment of block J, loaded once per 32-channel step.
-constexpr int job(int kind, int R, int J) { return (kind << 4) | (R << 2) | J; }
-constexpr int kNone = -1;
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives
+// element (i mod 4) of the 8 bytes addressed by lane (i/4 + 4j), j = 0..3.  frag8_tr builds,
+// from a row-major fp16 matrix M[k][m], the fragment in which lane l holds
+// M[k0 + 8 (l/16) + e][m0 + l%16], e = 0..7: lane s of a group supplies the addresses of 4
+// consecutive columns in rows k0 + 8 (l/16) + s/4 (+4).
+typedef short s4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4u frag8_tr(const _Float16* base, int ld, int k0, int m0, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+  const _Float16* a = base + (k0 + 8 * lg + (lr >> 2)) * ld + m0 + 4 * (lr & 3);
+  typedef unsigned u2 __attribute__((ext_vector_type(2)));
+  const u2 x = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(a)));
+  const u2 y = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(a + 4 * ld)));
+  return v4u{x[0], x[1], y[0], y[1]};
+}
+// One transpose read: the accumulator (column) layout of the 16x16 block at (r0, c0) of a
+// row-major fp16 matrix, lane l holding M[r0 + 4 (l/16) + e][c0 + l%16], e = 0..3.
+__device__ __forceinline__ h4 col_tr(const _Float16* base, int ld, int r0, int c0, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+  const _Float16* a = base + (r0 + 4 * lg + (lr >> 2)) * ld + c0 + 4 * (lr & 3);
+  return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(a)));
+}
 
-template <int J0, int J1, int J2, int J3>
-__device__ __forceinline__ void gram_jobs(Smem& sm, int b, int l) {
-  constexpr int jobs[4] = {J0, J1, J2, J3};
-  const int lr = l & 15, lg = l >> 4;
-  f4 acc[4];
+// ------------------------------------------------------------------------------------------
+// Role: state chain (waves 0, 1).  The wave owns value rows dv = c0 + 16 db + (0..15) and all
+// 128 key channels: St[kb] is the accumulator tile (d_k block kb, d_v block db) of S^T, lane
+// (lr, lg) holding S[dv = 16 db + lr][dk = 16 kb + 4 lg + e].  Two such tiles regroup in
+// registers into the 16x16x32 B operand (contraction over d_k) of X = K S^T; the accumulator
+// tiles of X, U and of the decayed U regroup the same way into the B operands of U = T X and of
+// the state update, whose A operand K^T comes from the row-major keys through transpose reads.
+__device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t bh, int c0, int db, int l,
+                                           int64_t nchunks) {
+  const int lr = l & 15, lg = l >> 4, dv = 16 * db + lr;
+  const int64_t T = p.T;
+  f4 St[8];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < 8; ++kb) {
+    f4 x = {0.f, 0.f, 0.f, 0.f};
+    if (p.s0) x = *reinterpret_cast<const f4*>(p.s0 + (bh * D + c0 + dv) * D + 16 * kb + 4 * lg);
+    St[kb] = x;
+  }
+  h8 Sb[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (jobs[t] == kNone) continue;
-      const int kind = jobs[t] >> 4, R = (jobs[t] >> 2) & 3, J = jobs[t] & 3;
-      const _Float16* Bm = kind ? &sm.q[0][0] : &sm.k[0][0];
-      acc[t] = mfma32(frag8(&sm.k[0][0], LQ, 16 * J, 32 * kk, l), frag8(Bm, LQ, 16 * R, 32 * kk, l), acc[t]);
-    }
+    Sb[kk] = pair_k32(to_h4(St[2 * kk]), to_h4(St[2 * kk + 1]));
+    *reinterpret_cast<h8*>(&sm.s[dv][32 * kk + 8 * lg]) = Sb[kk];
   }
-  const Gates& g = sm.gt[b];
+  __syncthreads();
+
+  for (int64_t c = -2; c < nchunks; ++c) {
+    h8 Ud[2];
+    float gC = 0.f;
+    if (c >= 0) {
+      const int b = (int)(c & 1), kb3 = kbuf(c);
+      const Gates& g = sm.gt[kb3];
+      f4 X[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (jobs[t] == kNone) continue;
-    const int kind = jobs[t] >> 4, R = (jobs[t] >> 2) & 3, J = jobs[t] & 3;
-    const int r = 16 * R + lr, j0 = 16 * J + 4 * lg;
-    if (kind == 1) {
-      *reinterpret_cast<h4*>(&sm.p[b][r][j0]) = to_h4(gram_scale<1>(g, R, J, lr, lg, acc[t]));
-    } else {
-      const f4 a = gram_scale<0>(g, R, J, lr, lg, acc[t]);
-      if (R == J)
-        invert_diag(sm, b, J, a, lr, lg);
-      else
-        *reinterpret_cast<h4*>(&sm.an[b][r][j0]) = to_h4(-a);
+      for (int i = 0; i < 4; ++i) X[i] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[i] = mfma32(lds8(&sm.k[kb3][16 * i + lr][32 * kk + 8 * lg]), Sb[kk], X[i]);
+      // lane: tokens 16 i + 4 lg + e, value channel dv
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * i + 4 * lg;
+        const f4 be = *reinterpret_cast<const f4*>(&g.beta[tok]);
+        const f4 ga = *reinterpret_cast<const f4*>(&g.gam[tok]);
+        const uint2 vv = *reinterpret_cast<const uint2*>(&sm.vt[b][dv][tok]);
+        const float v4[4] = {bf16_bits_to_f32(vv.x & 0xffffu), bf16_bits_to_f32(vv.x >> 16),
+                             bf16_bits_to_f32(vv.y & 0xffffu), bf16_bits_to_f32(vv.y >> 16)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[i][e] = be[e] * (v4[e] - ga[e] * X[i][e]);
+      }
+      const h8 Xb0 = pair_k32(to_h4(X[0]), to_h4(X[1])), Xb1 = pair_k32(to_h4(X[2]), to_h4(X[3]));
+      f4 U[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        U[i] = mfma32(lds8(&sm.t[b][16 * i + lr][8 * lg]), Xb0, f4{0.f, 0.f, 0.f, 0.f});
+        if (i >= 2) U[i] = mfma32(lds8(&sm.t[b][16 * i + lr][32 + 8 * lg]), Xb1, U[i]);
+      }
+      *reinterpret_cast<h8*>(&sm.u[dv][8 * lg]) = pair_k32(to_h4(U[0]), to_h4(U[1]));
+      *reinterpret_cast<h8*>(&sm.u[dv][32 + 8 * lg]) = pair_k32(to_h4(U[2]), to_h4(U[3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) U[i] *= *reinterpret_cast<const f4*>(&g.dec[16 * i + 4 * lg]);
+      Ud[0] = pair_k32(to_h4(U[0]), to_h4(U[1]));
+      Ud[1] = pair_k32(to_h4(U[2]), to_h4(U[3]));
+      gC = g.gam[C - 1];
     }
+    __syncthreads();
+    if (c >= 0) {
+      const int kb3 = kbuf(c);
+      const int64_t t0 = c * C;
+      const int n = (int)(T - t0 < C ? T - t0 : C);
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        f4 acc = St[kb] * gC;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+          acc = mfma32(__builtin_bit_cast(h8, frag8_tr(&sm.k[kb3][0][0], LQ, 32 * kc, 16 * kb, l)), Ud[kc], acc);
+        St[kb] = acc;
+      }
+      if (p.s_ckpt && n == C && ((t0 + n) % p.ckpt_every) == 0) {
+        const int64_t idx = (t0 + n) / p.ckpt_every - 1;
+        float* dst = p.s_ckpt + ((bh * p.n_ckpt + idx) * D + c0 + dv) * D + 4 * lg;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f4*>(dst + 16 * kb) = St[kb];
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        Sb[kk] = pair_k32(to_h4(St[2 * kk]), to_h4(St[2 * kk + 1]));
+        *reinterpret_cast<h8*>(&sm.s[dv][32 * kk + 8 * lg]) = Sb[kk];
+      }
+    }
+    __syncthreads();
+  }
+
+  if (p.s_final) {
+    float* dst = p.s_final + (bh * D + c0 + dv) * D + 4 * lg;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) *reinterpret_cast<f4*>(dst + 16 * kb) = St[kb];
   }
 }
 
-// Producer wavefronts 2..7: the 20 tiles of A and P plus the four diagonal inverses.
-__device__ __forceinline__ void produce(Smem& sm, int b, int w, int l) {
-  switch (w) {
-    case 2: gram_jobs<job(0, 0, 0), job(0, 1, 0), job(0, 2, 0), job(0, 3, 0)>(sm, b, l); break;
-    case 3: gram_jobs<job(1, 0, 0), job(1, 1, 0), job(1, 2, 0), job(1, 3, 0)>(sm, b, l); break;
-    case 4: gram_jobs<job(0, 1, 1), job(0, 2, 1), job(0, 3, 1), job(1, 1, 1)>(sm, b, l); break;
-    case 5: gram_jobs<job(1, 2, 1), job(1, 3, 1), job(0, 2, 2), kNone>(sm, b, l); break;
-    case 6: gram_jobs<job(1, 3, 2), job(0, 3, 3), kNone, kNone>(sm, b, l); break;
-    default: gram_jobs<job(1, 2, 2), job(0, 3, 2), job(1, 3, 3), kNone>(sm, b, l); break;
+// ------------------------------------------------------------------------------------------
+// Staging.  Global -> registers through buffer loads on per-stream buffer descriptors: the
+// hardware range check returns zeros for tokens outside the stream, which pads a ragged last
+// chunk with identity steps (k = v = q = 0, beta = 0, log alpha = 0) without branches.  The
+// staging roles run branch-free (chunks outside 0..nchunks-1 read as zeros and land in buffers
+// nobody reads at that point), so each wait names exactly the loads it needs and the prefetch
+// issued in the other phase stays in flight across the barriers (buffer loads never touch the
+// LDS counter the barriers wait on).
+
+// Role: outputs of token blocks tb0, tb0 + 1 (waves 4, 5), plus staging of half the queries
+// of the next chunk, and of its value slice (wave 4).
+// O^T tiles (d_v block d, token block tb): lane holds O[token 16 tb + lr][dv 16 d + 4 lg + e].
+// The outputs are written through a buffer descriptor, so rows outside the stream are dropped.
+template <typename TOut, int tb0>
+__device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, int64_t bh, int c0, int l, int64_t nchunks) {
+  constexpr int half = tb0 / 2;
+  const int lr = l & 15, lg = l >> 4;
+  const int64_t T = p.T, tok0 = bh * T;
+  const auto orr = __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<TOut*>(p.o) + tok0 * D), 0,
+                                                     (int)(T * D * (int64_t)sizeof(TOut)), kRsrcWord3);
+  const auto qr = stream_rsrc(p.q, tok0 * D, T * D);
+  const auto vr = stream_rsrc(p.v, tok0 * D, T * D);
+  const int ch = l & 15, rq = l >> 4;   // queries: 16-byte group ch of rows 32 half + 4 i + rq
+  const int dq = l & 3, vq = l >> 2;    // values: channels c0 + 8 dq .., tokens 4 vq .. 4 vq + 3
+  v4u qv[8], vv[4];
+  auto load_q = [&](int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = ld_b128(qr, (t0 + 32 * half + 4 * i + rq) * D + 8 * ch);
+    if constexpr (half == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[e] = ld_b128(vr, (t0 + 4 * vq + e) * D + c0 + 8 * dq);
+    }
+  };
+  load_q(-C);
+  __syncthreads();
+  for (int64_t c = -2; c < nchunks; ++c) {
+    const int b = (int)(c & 1), nb = b ^ 1;
+    f4 Oa[2][2];
+    // ---- phase 1: O = diag(gamma) Q S^T for chunk c; stage queries (and values) of chunk c + 1
+#pragma unroll
+    for (int t = 0; t < 2; ++t) Oa[t][0] = Oa[t][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      h8 qf[2], sf[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) qf[t] = lds8(&sm.q[b][16 * (tb0 + t) + lr][32 * kk + 8 * lg]);
+#pragma unroll
+      for (int d = 0; d < 2; ++d) sf[d] = lds8(&sm.s[16 * d + lr][32 * kk + 8 * lg]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int d = 0; d < 2; ++d) Oa[t][d] = mfma32(sf[d], qf[t], Oa[t][d]);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float ga = sm.gt[kbuf(c)].gam[16 * (tb0 + t) + lr];
+      Oa[t][0] *= ga;
+      Oa[t][1] *= ga;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<h8*>(&sm.q[nb][32 * half + 4 * i + rq][8 * ch]) = bf8_to_h8(qv[i]);
+    if constexpr (half == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // value channel 8 dq + e: tokens 4 vq .. 4 vq + 3 (bf16 bits)
+        uint2 o;
+        o.x = pick2(vv[0][e >> 1], vv[1][e >> 1], e);
+        o.y = pick2(vv[2][e >> 1], vv[3][e >> 1], e);
+        *reinterpret_cast<uint2*>(&sm.vt[nb][8 * dq + e][4 * vq]) = o;
+      }
+    }
+    load_q((c + 2) * C);
+    __syncthreads();
+    // ---- phase 2: O += P U, write o
+    const int64_t t0 = c * C;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int tb = tb0 + t;
+#pragma unroll
+      for (int kc = 0; kc <= (tb >> 1); ++kc) {  // P is zero above the diagonal blocks
+        const h8 pf = lds8(&sm.p[b][16 * tb + lr][32 * kc + 8 * lg]);
+#pragma unroll
+        for (int d = 0; d < 2; ++d) Oa[t][d] = mfma32(lds8(&sm.u[16 * d + lr][32 * kc + 8 * lg]), pf, Oa[t][d]);
+      }
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int off = (int)(((t0 + 16 * tb + lr) * D + c0 + 16 * d + 4 * lg) * (int64_t)sizeof(TOut));
+        if constexpr (sizeof(TOut) == 2) {
+          typedef unsigned u2v __attribute__((ext_vector_type(2)));
+          const u2v w = {pack_bf16x2(Oa[t][d][0], Oa[t][d][1]), pack_bf16x2(Oa[t][d][2], Oa[t][d][3])};
+          __builtin_amdgcn_raw_buffer_store_b64(w, orr, off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, Oa[t][d]), orr, off, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Role: diagonal of T (wave 2).  Phase 2 of iteration c forms the diagonal 16x16 blocks of A
+// of chunk c + 2 (decay factors, then the key Gram tiles) and stages them on the diagonal of
+// T's buffer; phase 1 of the next iteration replaces them by their inverses.
+__device__ __forceinline__ void tdiag_role(Smem& sm, int l, int64_t nchunks) {
+  const int lr = l & 15, lg = l >> 4;
+  __syncthreads();
+  for (int64_t c = -2; c < nchunks; ++c) {
+    {
+      const int nb = (int)((c + 1) & 1);
+      f4 rowN[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const h4 a = lds4(&sm.t[nb][16 * J + lr][16 * J + 4 * lg]);
+        rowN[J] = f4{(float)a[0], (float)a[1], (float)a[2], (float)a[3]};
+      }
+      h4 Tr[4], Tc[4];
+      invert_diag4(rowN, lr, lg, Tr, Tc);
+#pragma unroll
+      for (int J = 0; J < 4; ++J) *reinterpret_cast<h4*>(&sm.t[nb][16 * J + lr][16 * J + 4 * lg]) = Tr[J];
+    }
+    __syncthreads();
+    {
+      const int b2 = (int)(c & 1);  // buffer of chunk c + 2
+      const Gates& g = sm.gt[kbuf(c + 2)];
+      f4 dec[4], acc[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        dec[J] = g.beta[16 * J + lr] * diag_decay(g, J, lr, lg);
+        acc[J] = f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        h8 kf[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) kf[J] = lds8(&sm.k[kbuf(c + 2)][16 * J + lr][32 * kk + 8 * lg]);
+#pragma unroll
+        for (int J = 0; J < 4; ++J) acc[J] = mfma32(kf[J], kf[J], acc[J]);
+      }
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        f4 a = dec[J] * acc[J];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * lg + e == lr) a[e] = 0.f;  // strictly lower
+        *reinterpret_cast<h4*>(&sm.t[b2][16 * J + lr][16 * J + 4 * lg]) = to_h4(a);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Role: off-diagonal blocks of T for chunk c + 1 (wave 6, phase 2), by block forward
+// substitution down each column, T_ij = T_ii sum_{k=j}^{i-1} (-A_ik) T_kj, in rounds of
+// mutually independent blocks: (1,0) (2,1) (3,2), then (2,0) (3,1), then (3,0).  Phase 1
+// writes the gate tables of chunk c + 2.
+__device__ __forceinline__ void toff_role(Smem& sm, const ChunkArgs& p, int64_t bh, int l, int64_t nchunks) {
+  const int lr = l & 15, lg = l >> 4;
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  const int64_t tok0 = bh * p.T;
+  const auto br = stream_rsrc(p.beta, tok0, p.T);
+  const auto gr = stream_rsrc(p.log_alpha, tok0, p.T);
+  uint32_t bb, gg;
+  auto load_g = [&](int64_t t0) {
+    bb = __builtin_amdgcn_raw_buffer_load_b16(br, (int)((t0 + l) * 2), 0, 0);
+    gg = __builtin_amdgcn_raw_buffer_load_b16(gr, (int)((t0 + l) * 2), 0, 0);
+  };
+  load_g(0);
+  __syncthreads();
+  for (int64_t c = -2; c < nchunks; ++c) {
+    const int nb = (int)((c + 1) & 1);
+    // gate tables of chunk c + 2 (their buffer last held chunk c - 1)
+    {
+      const float x = wave_prefix_sum(bf16_bits_to_f32(gg & 0xffffu));
+      const float glast = __shfl(x, C - 1, 64);
+      const float gr1 = __shfl(x, 15, 64), gr2 = __shfl(x, 31, 64), gr3 = __shfl(x, 47, 64);
+      const int R = l >> 4;
+      const float gref = R == 0 ? 0.f : (R == 1 ? gr1 : (R == 2 ? gr2 : gr3));
+      const float beta = bf16_bits_to_f32(bb & 0xffffu);
+      Gates& gt = sm.gt[kbuf(c + 2)];
+      gt.G[l] = x;
+      gt.gam[l] = __expf(x);
+      gt.dec[l] = __expf(glast - x);
+      gt.beta[l] = beta;
+      const float el = __expf(x - gref);
+      gt.el[l] = el;
+      gt.nbel[l] = -beta * el;
+      gt.er[0][l] = __expf(fminf(gr1 - x, 0.f));
+      gt.er[1][l] = __expf(fminf(gr2 - x, 0.f));
+      gt.er[2][l] = __expf(fminf(gr3 - x, 0.f));
+      load_g((c + 3) * C);
+    }
+    __syncthreads();
+    h4 Tr[4], Tc[4], an[6];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      Tr[J] = lds4(&sm.t[nb][16 * J + lr][16 * J + 4 * lg]);
+      Tc[J] = col_tr(&sm.t[nb][0][0], LC, 16 * J, 16 * J, l);
+    }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) an[i] = lds4(&sm.an[i][lr][4 * lg]);
+    // lane holds col(T_ij): T[16 i + 4 lg + e][16 j + lr]
+    auto put = [&](int i, int j, h4 y) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.t[nb][16 * i + 4 * lg + e][16 * j + lr] = y[e];
+    };
+    h4 y10, y21, y32, y20, y31, y30;
+    {
+      const h4 z10 = to_h4(mfma16(an[an_idx(1, 0)], Tc[0], zero));
+      const h4 z21 = to_h4(mfma16(an[an_idx(2, 1)], Tc[1], zero));
+      const h4 z32 = to_h4(mfma16(an[an_idx(3, 2)], Tc[2], zero));
+      y10 = to_h4(mfma16(Tr[1], z10, zero));
+      y21 = to_h4(mfma16(Tr[2], z21, zero));
+      y32 = to_h4(mfma16(Tr[3], z32, zero));
+    }
+    {
+      const h4 z20 = to_h4(mfma16(an[an_idx(2, 1)], y10, mfma16(an[an_idx(2, 0)], Tc[0], zero)));
+      const h4 z31 = to_h4(mfma16(an[an_idx(3, 2)], y21, mfma16(an[an_idx(3, 1)], Tc[1], zero)));
+      y20 = to_h4(mfma16(Tr[2], z20, zero));
+      y31 = to_h4(mfma16(Tr[3], z31, zero));
+    }
+    {
+      const f4 z = mfma16(an[an_idx(3, 1)], y10, mfma16(an[an_idx(3, 0)], Tc[0], zero));
+      y30 = to_h4(mfma16(Tr[3], to_h4(mfma16(an[an_idx(3, 2)], y20, z)), zero));
+    }
+    put(1, 0, y10); put(2, 1, y21); put(3, 2, y32); put(2, 0, y20); put(3, 1, y31); put(3, 0, y30);
+    __syncthreads();
+  }
+}
+
+// Role: keys and P (wave 7).  Phase 1 converts and writes the row-major keys of chunk c + 2
+// (their buffer was last read in the previous phase 2); phase 2 computes
+// P = tril(Q K^T * D) of chunk c + 1, used by the outputs one iteration later.
+__device__ __forceinline__ void pgram_k_role(Smem& sm, const ChunkArgs& p, int64_t bh, int l, int64_t nchunks) {
+  const int lr = l & 15, lg = l >> 4;
+  constexpr int RR[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3}, JJ[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
+  const auto kr = stream_rsrc(p.k, bh * p.T * D, p.T * D);
+  const int ch = l & 15, rq = l >> 4;   // 16-byte group ch of rows 4 i + rq
+  v4u rows[16];
+  auto load_rows = [&](int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rows[i] = ld_b128(kr, (t0 + 4 * i + rq) * D + 8 * ch);
+  };
+  load_rows(0);
+  __syncthreads();
+  for (int64_t c = -2; c < nchunks; ++c) {
+    {
+      const int b = kbuf(c + 2);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) *reinterpret_cast<h8*>(&sm.k[b][4 * i + rq][8 * ch]) = bf8_to_h8(rows[i]);
+      load_rows((c + 3) * C);
+    }
+    __syncthreads();
+    const int nb = (int)((c + 1) & 1);
+    const Gates& g = sm.gt[kbuf(c + 1)];
+    f4 acc[10];
+#pragma unroll
+    for (int t = 0; t < 10; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      h8 kf[4], qf[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) kf[J] = lds8(&sm.k[kbuf(c + 1)][16 * J + lr][32 * kk + 8 * lg]);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) qf[R] = lds8(&sm.q[nb][16 * R + lr][32 * kk + 8 * lg]);
+#pragma unroll
+      for (int t = 0; t < 10; ++t) acc[t] = mfma32(kf[JJ[t]], qf[RR[t]], acc[t]);
+    }
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+      *reinterpret_cast<h4*>(&sm.p[nb][16 * J + lr][16 * J + 4 * lg]) = to_h4(diag_decay(g, J, lr, lg) * acc[J]);
+#pragma unroll
+    for (int t = 4; t < 10; ++t)
+      *reinterpret_cast<h4*>(&sm.p[nb][16 * RR[t] + lr][16 * JJ[t] + 4 * lg]) = to_h4(offdiag_p(g, RR[t], JJ[t], lr, lg, acc[t]));
+    __syncthreads();
+  }
+}
+
+// Role: off-diagonal A (wave 3, phase 1): the off-diagonal blocks of -A of chunk c + 1.
+__device__ __forceinline__ void aoff_role(Smem& sm, int l, int64_t nchunks) {
+  const int lr = l & 15, lg = l >> 4;
+  constexpr int RR[6] = {1, 2, 3, 2, 3, 3}, JJ[6] = {0, 0, 0, 1, 1, 2};
+  __syncthreads();
+  for (int64_t c = -2; c < nchunks; ++c) {
+    const Gates& g = sm.gt[kbuf(c + 1)];
+    f4 acc[6];
+#pragma unroll
+    for (int t = 0; t < 6; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      h8 kf[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) kf[J] = lds8(&sm.k[kbuf(c + 1)][16 * J + lr][32 * kk + 8 * lg]);
+#pragma unroll
+      for (int t = 0; t < 6; ++t) acc[t] = mfma32(kf[JJ[t]], kf[RR[t]], acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < 6; ++t)
+      *reinterpret_cast<h4*>(&sm.an[an_idx(RR[t], JJ[t])][lr][4 * lg]) = to_h4(offdiag_neg_a(g, RR[t], JJ[t], lr, lg, acc[t]));
+    __syncthreads();
+    __syncthreads();
   }
 }
 
@@ -273,193 +600,43 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int l = tid & 63;
+  const int l = tid & 63;
 
   // XCD-aware placement: consecutive workgroup ids are dealt round-robin over the 8 XCDs;
   // remap so the NT slices of a stream get ids that land on the same XCD.
   const unsigned nblk = gridDim.x;
   unsigned bid = blockIdx.x;
   if (nblk % (8 * NT) == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
-  const int tile = bid % NT;
+  const int c0 = (int)(bid % NT) * DVT;
   const int64_t bh = bid / NT;
-  const int c0 = tile * DVT;
-  const int64_t T = p.T;
-  const int64_t nchunks = (T + C - 1) / C;
+  const int64_t nchunks = (p.T + C - 1) / C;
 
-  // zero the never-written upper blocks of P and -A once
-  for (int e = tid; e < 2 * C * LC; e += NTH) {
-    (&sm.p[0][0][0])[e] = (_Float16)0.f;
-    (&sm.an[0][0][0])[e] = (_Float16)0.f;
-  }
+  // T and P start at zero; their upper blocks are never written
+  for (int e = tid; e < 2 * C * LC / 8; e += NTH) reinterpret_cast<v4u*>(&sm.t[0][0][0])[e] = v4u{0u, 0u, 0u, 0u};
+  for (int e = tid; e < 2 * C * LC / 8; e += NTH) reinterpret_cast<v4u*>(&sm.p[0][0][0])[e] = v4u{0u, 0u, 0u, 0u};
 
-  // state slice: wavefront w holds the S^T tiles (d_k block w, d_v block db): lane holds
-  // S[dv = 16 db + lr][dk = 16 w + 4 lg .. +3]
-  f4 S[2];
-  {
-    const int lr = l & 15, lg = l >> 4;
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const int dk = 16 * w + 4 * lg, dv = 16 * db + lr;
-      f4 x = {0.f, 0.f, 0.f, 0.f};
-      if (p.s0) x = *reinterpret_cast<const f4*>(p.s0 + (bh * D + c0 + dv) * D + dk);
-      S[db] = x;
-      *reinterpret_cast<h4*>(&sm.s[dv][dk]) = to_h4(x);
-    }
-  }
-
-  const Streams sr = make_streams(p, bh, tid >= 256);
-  Stage st;
-  if (nchunks > 0) {
-    stage_load(st, sr, 0, tid, c0);
-    __syncthreads();  // P / -A zeroed before the producers write into them
-    stage_store(st, sm, 0, tid);
-    if (nchunks > 1) stage_load(st, sr, C, tid, c0);
-    __syncthreads();
-    if (w >= 2) produce(sm, 0, w, l);
-    __syncthreads();
-  }
-
-  TOut* O = static_cast<TOut*>(p.o);
-  for (int64_t ci = 0; ci < nchunks; ++ci) {
-    const int cb = (int)(ci & 1), nb = cb ^ 1;
-    const int64_t t0 = ci * C;
-    const int n = (int)(T - t0 < C ? T - t0 : C);
-    const Gates& gc = sm.gt[cb];
-
-    // ---- A: X tiles (waves 0,1: value block db = w) and O = diag(gamma) Q S^T (waves 2..5:
-    // token block w - 2, both value blocks)
-    l = opaque(l);
-    int lr = l & 15, lg = l >> 4;
-    f4 X[4], Oacc[2];
-    if (w < 2) {
-      const int db = w, dv = 16 * db + lr;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) X[i] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const h8 sb = frag8(&sm.s[0][0], LQ, 16 * db, 32 * kk, l);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) X[i] = mfma32(frag8(&sm.k[0][0], LQ, 16 * i, 32 * kk, l), sb, X[i]);
-      }
-      // lane: token c = 16 i + 4 lg + e, value channel dv
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 16 * i + 4 * lg;
-        const f4 be = *reinterpret_cast<const f4*>(&gc.beta[c]);
-        const f4 ga = *reinterpret_cast<const f4*>(&gc.gam[c]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) X[i][e] = be[e] * ((float)sm.v[c + e][dv] - ga[e] * X[i][e]);
-      }
-    } else if (w < 6) {
-      const int cbk = w - 2;
-      Oacc[0] = Oacc[1] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const h8 qb = frag8(&sm.q[0][0], LQ, 16 * cbk, 32 * kk, l);
-#pragma unroll
-        for (int db = 0; db < 2; ++db) Oacc[db] = mfma32(frag8(&sm.s[0][0], LQ, 16 * db, 32 * kk, l), qb, Oacc[db]);
-      }
-      // lane: value channel dv = 16 db + 4 lg + e, token c = 16 cbk + lr
-      const float ga = gc.gam[16 * cbk + lr];
-      Oacc[0] *= ga;
-      Oacc[1] *= ga;
-    }
-    __syncthreads();
-
-    // ---- S: stage chunk ci+1 into the other buffer, prefetch chunk ci+2
-    if (ci + 1 < nchunks) {
-      stage_store(st, sm, nb, tid);
-      if (ci + 2 < nchunks) stage_load(st, sr, t0 + 2 * C, tid, c0);
-    }
-    __syncthreads();
-
-    // ---- B: substitution of chunk ci (waves 0,1); A, P, T_ii of chunk ci+1 (waves 2..7)
-    l = opaque(l);
-    lr = l & 15, lg = l >> 4;
-    if (w < 2) {
-      const int db = w, dv = 16 * db + lr;
-      h4 an[6], tdf[4];
-#pragma unroll
-      for (int i = 0, m = 0; i < 4; ++i) {
-        tdf[i] = frag4(&sm.td[cb][i][0][0], LT, 0, 0, l);
-#pragma unroll
-        for (int j = 0; j < i; ++j, ++m) an[m] = frag4(&sm.an[cb][0][0], LC, 16 * i, 16 * j, l);
-      }
-      h4 Uh[4];
-#pragma unroll
-      for (int i = 0, m = 0; i < 4; ++i) {
-        f4 acc = X[i];
-#pragma unroll
-        for (int j = 0; j < i; ++j, ++m) acc = mfma16(an[m], Uh[j], acc);
-        const f4 U = mfma16(tdf[i], to_h4(acc), f4{0.f, 0.f, 0.f, 0.f});
-        Uh[i] = to_h4(U);
-        // lane: token c = 16 i + 4 lg + e, value channel dv
-        const int cbase = 16 * i + 4 * lg;
-        *reinterpret_cast<h4*>(&sm.u[dv][cbase]) = Uh[i];
-        *reinterpret_cast<h4*>(&sm.ud[dv][cbase]) = to_h4(U * *reinterpret_cast<const f4*>(&gc.dec[cbase]));
-      }
-    } else if (ci + 1 < nchunks) {
-      produce(sm, nb, w, l);
-    }
-    __syncthreads();
-
-    // ---- C: O += U^T P^T and the output (waves 2..5); the state hand-off (all)
-    l = opaque(l);
-    lr = l & 15, lg = l >> 4;
-    if (w >= 2 && w < 6) {
-      const int cbk = w - 2;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        if (kc == 1 && cbk < 2) continue;
-        const h8 pb = frag8(&sm.p[cb][0][0], LC, 16 * cbk, 32 * kc, l);
-#pragma unroll
-        for (int db = 0; db < 2; ++db) Oacc[db] = mfma32(frag8(&sm.u[0][0], LC, 16 * db, 32 * kc, l), pb, Oacc[db]);
-      }
-      const int c = 16 * cbk + lr;
-      if (c < n) {
-#pragma unroll
-        for (int db = 0; db < 2; ++db) store_o4<TOut>(O, (bh * T + t0 + c) * D + c0 + 16 * db + 4 * lg, Oacc[db]);
-      }
-    }
-    {
-      const float glast = gc.gam[C - 1];
-      const bool snap = p.s_ckpt && n == C && ((t0 + n) % p.ckpt_every) == 0;
-      const int dkr = 16 * w + lr;  // key channel of this lane's A-operand row
-      h8 ka[2];
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) ka[kc] = *reinterpret_cast<const h8*>(&sm.kt[cb][dkr][kt_col(dkr, 32 * kc + 8 * lg)]);
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        f4 acc = S[db] * glast;
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) acc = mfma32(ka[kc], frag8(&sm.ud[0][0], LC, 16 * db, 32 * kc, l), acc);
-        S[db] = acc;
-        const int dk = 16 * w + 4 * lg, dv = 16 * db + lr;
-        *reinterpret_cast<h4*>(&sm.s[dv][dk]) = to_h4(acc);
-        if (snap) {
-          const int64_t idx = (t0 + n) / p.ckpt_every - 1;
-          *reinterpret_cast<f4*>(p.s_ckpt + ((bh * p.n_ckpt + idx) * D + c0 + dv) * D + dk) = acc;
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  if (p.s_final) {
-    const int lr = l & 15, lg = l >> 4;
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const int dk = 16 * w + 4 * lg, dv = 16 * db + lr;
-      *reinterpret_cast<f4*>(p.s_final + (bh * D + c0 + dv) * D + dk) = S[db];
-    }
+  // Every role runs nchunks + 2 iterations of two barriers after one initial barrier.  Waves w
+  // and w + 4 share a SIMD: the chains (0, 1) share theirs with the outputs (4, 5).
+  switch (w) {
+    case 0:
+    case 1:
+      __builtin_amdgcn_s_setprio(2);
+      chain_role(sm, p, bh, c0, w, l, nchunks);
+      break;
+    case 2: tdiag_role(sm, l, nchunks); break;
+    case 3: aoff_role(sm, l, nchunks); break;
+    case 4: out_role<TOut, 0>(sm, p, bh, c0, l, nchunks); break;
+    case 5: out_role<TOut, 2>(sm, p, bh, c0, l, nchunks); break;
+    case 6: toff_role(sm, p, bh, l, nchunks); break;
+    default: pgram_k_role(sm, p, bh, l, nchunks); break;
   }
 }
 
 }  // namespace
 
 bool chunk_mfma_supported(const ChunkArgs& a) {
-  // buffer-descriptor offsets are 32-bit: one stream's q/k/v must stay under 2 GiB
-  return a.in_dtype == GDN_BF16 && a.D == D && a.chunk == C && a.T * D * 2 < (INT64_C(1) << 31);
+  // buffer-descriptor offsets are 32-bit: one stream's q/k/v and o must stay under 2 GiB
+  return a.in_dtype == GDN_BF16 && a.D == D && a.chunk == C && a.T * D * 4 < (INT64_C(1) << 31);
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool kda, hipStream_t s) {

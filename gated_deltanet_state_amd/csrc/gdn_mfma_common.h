@@ -45,6 +45,28 @@ __device__ __forceinline__ h4 frag4(const _Float16* base, int ld, int m0, int k0
 // 8 apart, same tokens) spread over the LDS banks; 16-byte reads stay contiguous.
 __device__ __forceinline__ int kt_col(int dk, int c) { return (((c >> 3) ^ ((dk >> 3) & 7)) << 3) | (c & 7); }
 
+// Two accumulator-layout 16x16 tiles t0 (rows 0..15) and t1 (rows 16..31) of a 32-row block,
+// rounded to fp16, regrouped in registers into the 16x16x32 operand layout in which the 32
+// rows are the contraction index: lane (column c, group g) receives rows 8g .. 8g+7 of
+// column c.  In a tile, lane group g holds rows 4g .. 4g+3; per dword, one permlane32 swap
+// and one permlane16 swap (gfx950) bring them to the lane groups that need them:
+//   (A0 A1 A2 A3), (B0 B1 B2 B3) -> (A0 A1 B0 B1), (A2 A3 B2 B3) -> (A0 A2 B0 B2), (A1 A3 B1 B3)
+// where Xg is the value of lane group g; the first result holds rows 8g..8g+3, the second
+// rows 8g+4..8g+7.
+__device__ __forceinline__ h8 pair_k32(h4 t0, h4 t1) {
+  typedef unsigned u2 __attribute__((ext_vector_type(2)));
+  const u2 a = __builtin_bit_cast(u2, t0), b = __builtin_bit_cast(u2, t1);
+  v4u r;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const u2 s32 = __builtin_amdgcn_permlane32_swap(a[d], b[d], false, false);
+    const u2 s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+    r[d] = s16[0];
+    r[2 + d] = s16[1];
+  }
+  return __builtin_bit_cast(h8, r);
+}
+
 __device__ __forceinline__ h4 to_h4(f4 x) {
   h4 r;
   r[0] = (_Float16)x[0]; r[1] = (_Float16)x[1]; r[2] = (_Float16)x[2]; r[3] = (_Float16)x[3];
