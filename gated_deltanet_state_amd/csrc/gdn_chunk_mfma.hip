@@ -50,7 +50,7 @@ constexpr int D = 128;       // head dimension (d_k = d_v)
 constexpr int C = 64;        // chunk length
 constexpr int DVT = 32;      // value rows per workgroup
 constexpr int NT = D / DVT;  // workgroups per stream
-constexpr int NTH = 512;     // threads per workgroup (8 wavefronts)
+constexpr int NTH = 768;     // threads per workgroup (12 wavefronts)
 constexpr int LQ = D + 16;   // row stride (halves) of [token][channel] tiles: 288 bytes = 72 banks
 constexpr int LC = C + 8;    // row stride (halves) of [channel][token] and [token][token] tiles
 constexpr int LT = 24;       // row stride (halves) of 16x16 blocks
@@ -64,21 +64,24 @@ struct alignas(16) Gates {
   alignas(16) float el[C];    // e^{G_r - G_ref(block of r)}, G_ref(R) = G_{16R-1} (0 for R = 0)
   alignas(16) float nbel[C];  // -beta_r el_r
   alignas(16) float er[3][C]; // er[R-1][j] = e^{G_ref(R) - G_j} for j < 16 R, R = 1..3
+  alignas(16) _Float16 bbg[C][2];  // (beta_r, beta_r gamma_r) in fp16, read by the state chain
 };
 
-// Buffers hold data of one chunk: keys and gate tables by chunk mod 3, the others by chunk
-// mod 2.  Bank
-// layout (gfx950 LDS: 16-byte accesses are served 32 lanes at a time over 128 four-byte banks):
-// a 16-row x 32-column fragment read is conflict-free when the row stride is an odd multiple
-// of 8 banks, hence the 288-byte rows of the [token][channel] tiles.
+// Buffers hold data of one chunk: keys and gate tables by chunk mod 3, T by chunk mod 2, the
+// others single.  Bank layout (gfx950 LDS: 16-byte accesses are served 32 lanes at a time over
+// 128 four-byte banks): a 16-row x 32-column fragment read is conflict-free when the row stride
+// is an odd multiple of 8 banks, hence the 288-byte rows of the [token][channel] tiles and the
+// 160-byte rows of the transposed keys.
+constexpr int LK = C + 16;   // row stride (halves) of the transposed keys
 struct alignas(16) Smem {
   alignas(16) _Float16 k[3][C][LQ];      // keys                                  [token][d_k]
-  alignas(16) _Float16 q[2][C][LQ];      // queries                               [token][d_k]
+  alignas(16) _Float16 q[C][LQ];         // queries                               [token][d_k]
   alignas(16) _Float16 s[DVT][LQ];       // fp16 state slice entering the chain's chunk [d_v][d_k]
-  alignas(16) uint16_t vt[2][DVT][LC];   // value slice, bf16 bits                [d_v][token]
+  alignas(16) _Float16 kt[D][LK];        // keys scaled by e^{G_63 - G}, transposed [d_k][token]
+  alignas(16) uint16_t vt[DVT][LC];      // value slice, bf16 bits                [d_v][token]
   alignas(16) _Float16 t[2][C][LC];      // T = (I + A)^{-1}, upper blocks zero; A_JJ staged on the diagonal
-  alignas(16) _Float16 p[2][C][LC];      // tril(Q K^T * D), upper blocks zero     [token][token]
-  alignas(16) _Float16 an[6][16][LT];    // -A, off-diagonal blocks (R, J), R > J
+  alignas(16) _Float16 p[C][LC];         // tril(Q K^T * D), upper blocks zero     [token][token]
+  alignas(16) _Float16 an[2][6][16][LT]; // -A, off-diagonal blocks (R, J), R > J, by chunk mod 2
   alignas(16) _Float16 u[DVT][LC];       // U of the chain's chunk                [d_v][token]
   alignas(16) Gates gt[3];
 };
@@ -126,48 +129,46 @@ __device__ __forceinline__ f4 diag_decay(const Gates& g, int J, int lr, int lg) 
   return f;
 }
 
-// Inverses of the four unit lower-triangular diagonal blocks (I + N_J), N_J = A_JJ strictly
-// lower, as (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0) on 16x16x16 MFMAs.  With row(M)
-// (lane holds M[lr][4lg..+3], the A-operand layout) and col(M) (lane holds M[4lg..+3][lr], the
-// B-operand and accumulator layout): col(XY) = mfma(row X, col Y) and row(XY) = mfma(col Y,
-// row X); in particular col(N) = mfma(row N, col I).  Returns each inverse in both layouts
-// (the factors commute, so either order is the product).  The four chains are independent
-// and advance level by level so their MFMA latencies overlap.
-__device__ __forceinline__ void invert_diag4(const f4 (&rowN)[4], int lr, int lg, h4 (&Tr)[4], h4 (&Tc)[4]) {
+// Inverses of NB unit lower-triangular diagonal blocks (I + N_J), N_J = A_JJ strictly lower,
+// as (I - N)(I + N^2)(I + N^4)(I + N^8) (N^16 = 0) on 16x16x16 MFMAs.  With row(M) (lane holds
+// M[lr][4lg..+3], the A-operand layout) and col(M) (lane holds M[4lg..+3][lr], the B-operand
+// and accumulator layout): col(XY) = mfma(row X, col Y) and row(XY) = mfma(col Y, row X); in
+// particular col(N) = mfma(row N, col I).  Returns each inverse in row layout (the factors
+// commute, so either order is the product).  The chains are independent and advance level by
+// level so their MFMA latencies overlap.
+template <int NB>
+__device__ __forceinline__ void invert_diag(const f4 (&rowN)[NB], int lr, int lg, h4 (&Tr)[NB]) {
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
   f4 eye;  // identity in either layout: element i of lane (lr, lg) is on the diagonal iff 4 lg + i == lr
 #pragma unroll
   for (int i = 0; i < 4; ++i) eye[i] = (4 * lg + i == lr) ? 1.f : 0.f;
   const h4 eyeh = to_h4(eye);
-  h4 rN[4], cN[4], n2ch[4], n2rh[4], n4ch[4], n4rh[4], p1[4], n8e[4], p2r[4];
-  f4 n2c[4], n4c[4];
+  h4 rN[NB], cN[NB], n2ch[NB], n2rh[NB], n4ch[NB], n4rh[NB], p1[NB], n8e[NB], p2r[NB];
+  f4 n2c[NB], n4c[NB];
 #pragma unroll
-  for (int J = 0; J < 4; ++J) rN[J] = to_h4(rowN[J]);
+  for (int J = 0; J < NB; ++J) rN[J] = to_h4(rowN[J]);
 #pragma unroll
-  for (int J = 0; J < 4; ++J) cN[J] = to_h4(mfma16(rN[J], eyeh, zero));
+  for (int J = 0; J < NB; ++J) cN[J] = to_h4(mfma16(rN[J], eyeh, zero));
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
+  for (int J = 0; J < NB; ++J) {
     n2c[J] = mfma16(rN[J], cN[J], zero);
     n2rh[J] = to_h4(mfma16(cN[J], rN[J], zero));
   }
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
+  for (int J = 0; J < NB; ++J) {
     n2ch[J] = to_h4(n2c[J]);
     n4c[J] = mfma16(n2rh[J], n2ch[J], zero);
     n4rh[J] = to_h4(mfma16(n2ch[J], n2rh[J], zero));
     p1[J] = to_h4(mfma16(to_h4(n2c[J] + eye), to_h4(eye - rowN[J]), zero));   // row((I - N)(I + N^2))
   }
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
+  for (int J = 0; J < NB; ++J) {
     n4ch[J] = to_h4(n4c[J]);
     n8e[J] = to_h4(mfma16(n4rh[J], n4ch[J], zero) + eye);                     // col(I + N^8)
     p2r[J] = to_h4(mfma16(to_h4(n4c[J] + eye), p1[J], zero));                 // row(P1 (I + N^4))
   }
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    Tr[J] = to_h4(mfma16(n8e[J], p2r[J], zero));                              // row(P2 (I + N^8))
-    Tc[J] = to_h4(mfma16(p2r[J], n8e[J], zero));                              // col(P2 (I + N^8))
-  }
+  for (int J = 0; J < NB; ++J) Tr[J] = to_h4(mfma16(n8e[J], p2r[J], zero));   // row(P2 (I + N^8))
 }
 
 // LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives
@@ -197,8 +198,10 @@ __device__ __forceinline__ h4 col_tr(const _Float16* base, int ld, int r0, int c
 // 128 key channels: St[kb] is the accumulator tile (d_k block kb, d_v block db) of S^T, lane
 // (lr, lg) holding S[dv = 16 db + lr][dk = 16 kb + 4 lg + e].  Two such tiles regroup in
 // registers into the 16x16x32 B operand (contraction over d_k) of X = K S^T; the accumulator
-// tiles of X, U and of the decayed U regroup the same way into the B operands of U = T X and of
-// the state update, whose A operand K^T comes from the row-major keys through transpose reads.
+// tiles of X and U regroup the same way into the B operands of U = T X and of the state update
+// S^T <- gamma_63 S^T + (diag(e^{G_63 - G}) K)^T U.  Its A operand, the decayed transposed keys,
+// is staged by the output waves in two halves: tokens 0..31 one phase ahead (fetched with the
+// other phase-1 operands) and tokens 32..63 in phase 1 (fetched at the start of phase 2).
 __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t bh, int c0, int db, int l,
                                            int64_t nchunks) {
   const int lr = l & 15, lg = l >> 4, dv = 16 * db + lr;
@@ -219,11 +222,19 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
   __syncthreads();
 
   for (int64_t c = -2; c < nchunks; ++c) {
-    h8 Ud[2];
-    float gC = 0.f;
+    h8 Ub[2], kt0[8];
     if (c >= 0) {
-      const int b = (int)(c & 1), kb3 = kbuf(c);
+      const int kb3 = kbuf(c);
       const Gates& g = sm.gt[kb3];
+      h8 bg[4];    // (beta, beta gamma) of tokens 16 i + 4 lg + e
+      uint2 vv[4]; // values of those tokens, bf16
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bg[i] = lds8(&g.bbg[16 * i + 4 * lg][0]);
+        vv[i] = *reinterpret_cast<const uint2*>(&sm.vt[dv][16 * i + 4 * lg]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) kt0[kb] = lds8(&sm.kt[16 * kb + lr][8 * lg]);
       f4 X[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) X[i] = f4{0.f, 0.f, 0.f, 0.f};
@@ -231,46 +242,38 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[i] = mfma32(lds8(&sm.k[kb3][16 * i + lr][32 * kk + 8 * lg]), Sb[kk], X[i]);
-      // lane: tokens 16 i + 4 lg + e, value channel dv
+      // lane: tokens 16 i + 4 lg + e, value channel dv; X = beta v - beta gamma (K S^T)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = 16 * i + 4 * lg;
-        const f4 be = *reinterpret_cast<const f4*>(&g.beta[tok]);
-        const f4 ga = *reinterpret_cast<const f4*>(&g.gam[tok]);
-        const uint2 vv = *reinterpret_cast<const uint2*>(&sm.vt[b][dv][tok]);
-        const float v4[4] = {bf16_bits_to_f32(vv.x & 0xffffu), bf16_bits_to_f32(vv.x >> 16),
-                             bf16_bits_to_f32(vv.y & 0xffffu), bf16_bits_to_f32(vv.y >> 16)};
+        const float v4[4] = {bf16_bits_to_f32(vv[i].x & 0xffffu), bf16_bits_to_f32(vv[i].x >> 16),
+                             bf16_bits_to_f32(vv[i].y & 0xffffu), bf16_bits_to_f32(vv[i].y >> 16)};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[i][e] = be[e] * (v4[e] - ga[e] * X[i][e]);
+        for (int e = 0; e < 4; ++e) X[i][e] = (float)bg[i][2 * e] * v4[e] - (float)bg[i][2 * e + 1] * X[i][e];
       }
       const h8 Xb0 = pair_k32(to_h4(X[0]), to_h4(X[1])), Xb1 = pair_k32(to_h4(X[2]), to_h4(X[3]));
       f4 U[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        U[i] = mfma32(lds8(&sm.t[b][16 * i + lr][8 * lg]), Xb0, f4{0.f, 0.f, 0.f, 0.f});
-        if (i >= 2) U[i] = mfma32(lds8(&sm.t[b][16 * i + lr][32 + 8 * lg]), Xb1, U[i]);
+        U[i] = mfma32(lds8(&sm.t[(int)(c & 1)][16 * i + lr][8 * lg]), Xb0, f4{0.f, 0.f, 0.f, 0.f});
+        if (i >= 2) U[i] = mfma32(lds8(&sm.t[(int)(c & 1)][16 * i + lr][32 + 8 * lg]), Xb1, U[i]);
       }
-      *reinterpret_cast<h8*>(&sm.u[dv][8 * lg]) = pair_k32(to_h4(U[0]), to_h4(U[1]));
-      *reinterpret_cast<h8*>(&sm.u[dv][32 + 8 * lg]) = pair_k32(to_h4(U[2]), to_h4(U[3]));
+      Ub[0] = pair_k32(to_h4(U[0]), to_h4(U[1]));
+      Ub[1] = pair_k32(to_h4(U[2]), to_h4(U[3]));
+      *reinterpret_cast<h8*>(&sm.u[dv][8 * lg]) = Ub[0];
+      *reinterpret_cast<h8*>(&sm.u[dv][32 + 8 * lg]) = Ub[1];
+      const float gC = g.gam[C - 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) U[i] *= *reinterpret_cast<const f4*>(&g.dec[16 * i + 4 * lg]);
-      Ud[0] = pair_k32(to_h4(U[0]), to_h4(U[1]));
-      Ud[1] = pair_k32(to_h4(U[2]), to_h4(U[3]));
-      gC = g.gam[C - 1];
+      for (int kb = 0; kb < 8; ++kb) St[kb] *= gC;
     }
     __syncthreads();
     if (c >= 0) {
-      const int kb3 = kbuf(c);
       const int64_t t0 = c * C;
       const int n = (int)(T - t0 < C ? T - t0 : C);
+      h8 kt1[8];
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        f4 acc = St[kb] * gC;
+      for (int kb = 0; kb < 8; ++kb) kt1[kb] = lds8(&sm.kt[16 * kb + lr][32 + 8 * lg]);
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-          acc = mfma32(__builtin_bit_cast(h8, frag8_tr(&sm.k[kb3][0][0], LQ, 32 * kc, 16 * kb, l)), Ud[kc], acc);
-        St[kb] = acc;
-      }
+      for (int kb = 0; kb < 8; ++kb) St[kb] = mfma32(kt1[kb], Ub[1], mfma32(kt0[kb], Ub[0], St[kb]));
       if (p.s_ckpt && n == C && ((t0 + n) % p.ckpt_every) == 0) {
         const int64_t idx = (t0 + n) / p.ckpt_every - 1;
         float* dst = p.s_ckpt + ((bh * p.n_ckpt + idx) * D + c0 + dv) * D + 4 * lg;
@@ -302,43 +305,62 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
 // issued in the other phase stays in flight across the barriers (buffer loads never touch the
 // LDS counter the barriers wait on).
 
-// Role: outputs of token blocks tb0, tb0 + 1 (waves 4, 5), plus staging of half the queries
-// of the next chunk, and of its value slice (wave 4).
-// O^T tiles (d_v block d, token block tb): lane holds O[token 16 tb + lr][dv 16 d + 4 lg + e].
-// The outputs are written through a buffer descriptor, so rows outside the stream are dropped.
+// Half of the row-major tokens of a chunk (rows 32 half + 0..31) of a [token][d_k] bf16 input,
+// converted to fp16 into an LDS tile.
+template <int half>
+struct RowStage {
+  __amdgpu_buffer_rsrc_t r;
+  v4u x[8];
+  int ch, rq;
+  __device__ __forceinline__ RowStage(const void* base, const ChunkArgs& p, int64_t bh, int l)
+      : r(stream_rsrc(base, bh * p.T * D, p.T * D)), ch(l & 15), rq(l >> 4) {}
+  __device__ __forceinline__ void load(int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = ld_b128(r, (t0 + 32 * half + 4 * i + rq) * D + 8 * ch);
+  }
+  __device__ __forceinline__ void store(_Float16 (*dst)[LQ]) const {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<h8*>(&dst[32 * half + 4 * i + rq][8 * ch]) = bf8_to_h8(x[i]);
+  }
+};
+
+// Decayed, transposed keys for 4 d_k blocks kb0.. and one 32-token half kc of a chunk: transpose
+// reads from the row-major keys, each token scaled by e^{G_63 - G}.
+__device__ __forceinline__ void stage_kt(Smem& sm, const _Float16* k, const Gates& g, int kb0, int kc, int l) {
+  const int lr = l & 15, lg = l >> 4;
+  const h4 a = to_h4(*reinterpret_cast<const f4*>(&g.dec[32 * kc + 8 * lg]));
+  const h4 b = to_h4(*reinterpret_cast<const f4*>(&g.dec[32 * kc + 8 * lg + 4]));
+  const h8 dech = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int dk0 = 16 * (kb0 + j);
+    const h8 x = __builtin_bit_cast(h8, frag8_tr(k, LQ, 32 * kc, dk0, l)) * dech;
+    *reinterpret_cast<h8*>(&sm.kt[dk0 + lr][32 * kc + 8 * lg]) = x;
+  }
+}
+
+// Role: outputs of token blocks tb0, tb0 + 1 (waves 4, 5).  O^T tiles (d_v block d, token block
+// tb): lane holds O[token 16 tb + lr][dv 16 d + 4 lg + e], written through a buffer descriptor
+// so rows outside the stream are dropped.  The wave also stages the decayed transposed keys of
+// d_k blocks 2 tb0 .. 2 tb0 + 3: tokens 32..63 of chunk c in phase 1 and tokens 0..31 of chunk
+// c + 1 in phase 2 (each half is read by the chain in the phase after it is written).
 template <typename TOut, int tb0>
 __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, int64_t bh, int c0, int l, int64_t nchunks) {
-  constexpr int half = tb0 / 2;
   const int lr = l & 15, lg = l >> 4;
   const int64_t T = p.T, tok0 = bh * T;
   const auto orr = __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<TOut*>(p.o) + tok0 * D), 0,
                                                      (int)(T * D * (int64_t)sizeof(TOut)), kRsrcWord3);
-  const auto qr = stream_rsrc(p.q, tok0 * D, T * D);
-  const auto vr = stream_rsrc(p.v, tok0 * D, T * D);
-  const int ch = l & 15, rq = l >> 4;   // queries: 16-byte group ch of rows 32 half + 4 i + rq
-  const int dq = l & 3, vq = l >> 2;    // values: channels c0 + 8 dq .., tokens 4 vq .. 4 vq + 3
-  v4u qv[8], vv[4];
-  auto load_q = [&](int64_t t0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qv[i] = ld_b128(qr, (t0 + 32 * half + 4 * i + rq) * D + 8 * ch);
-    if constexpr (half == 0) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vv[e] = ld_b128(vr, (t0 + 4 * vq + e) * D + c0 + 8 * dq);
-    }
-  };
-  load_q(-C);
   __syncthreads();
   for (int64_t c = -2; c < nchunks; ++c) {
-    const int b = (int)(c & 1), nb = b ^ 1;
     f4 Oa[2][2];
-    // ---- phase 1: O = diag(gamma) Q S^T for chunk c; stage queries (and values) of chunk c + 1
+    // ---- phase 1: O = diag(gamma) Q S^T for chunk c
 #pragma unroll
     for (int t = 0; t < 2; ++t) Oa[t][0] = Oa[t][1] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       h8 qf[2], sf[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) qf[t] = lds8(&sm.q[b][16 * (tb0 + t) + lr][32 * kk + 8 * lg]);
+      for (int t = 0; t < 2; ++t) qf[t] = lds8(&sm.q[16 * (tb0 + t) + lr][32 * kk + 8 * lg]);
 #pragma unroll
       for (int d = 0; d < 2; ++d) sf[d] = lds8(&sm.s[16 * d + lr][32 * kk + 8 * lg]);
 #pragma unroll
@@ -352,27 +374,16 @@ __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, int64_t b
       Oa[t][0] *= ga;
       Oa[t][1] *= ga;
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<h8*>(&sm.q[nb][32 * half + 4 * i + rq][8 * ch]) = bf8_to_h8(qv[i]);
-    if constexpr (half == 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {  // value channel 8 dq + e: tokens 4 vq .. 4 vq + 3 (bf16 bits)
-        uint2 o;
-        o.x = pick2(vv[0][e >> 1], vv[1][e >> 1], e);
-        o.y = pick2(vv[2][e >> 1], vv[3][e >> 1], e);
-        *reinterpret_cast<uint2*>(&sm.vt[nb][8 * dq + e][4 * vq]) = o;
-      }
-    }
-    load_q((c + 2) * C);
+    stage_kt(sm, &sm.k[kbuf(c)][0][0], sm.gt[kbuf(c)], 2 * tb0, 1, l);
     __syncthreads();
-    // ---- phase 2: O += P U, write o
+    // ---- phase 2: O += P U, write o; transposed keys (tokens 0..31) of chunk c + 1
     const int64_t t0 = c * C;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int tb = tb0 + t;
 #pragma unroll
       for (int kc = 0; kc <= (tb >> 1); ++kc) {  // P is zero above the diagonal blocks
-        const h8 pf = lds8(&sm.p[b][16 * tb + lr][32 * kc + 8 * lg]);
+        const h8 pf = lds8(&sm.p[16 * tb + lr][32 * kc + 8 * lg]);
 #pragma unroll
         for (int d = 0; d < 2; ++d) Oa[t][d] = mfma32(lds8(&sm.u[16 * d + lr][32 * kc + 8 * lg]), pf, Oa[t][d]);
       }
@@ -388,81 +399,141 @@ __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, int64_t b
         }
       }
     }
+    stage_kt(sm, &sm.k[kbuf(c + 1)][0][0], sm.gt[kbuf(c + 1)], 2 * tb0, 0, l);
     __syncthreads();
   }
 }
 
-// Role: diagonal of T (wave 2).  Phase 2 of iteration c forms the diagonal 16x16 blocks of A
-// of chunk c + 2 (decay factors, then the key Gram tiles) and stages them on the diagonal of
-// T's buffer; phase 1 of the next iteration replaces them by their inverses.
+// Role: diagonal of T, blocks J0 and J0 + 1 (waves 2, 3).  Phase 2 of iteration c forms the
+// diagonal 16x16 blocks of A of chunk c + 2 (decay factors, then the key Gram tiles) and stages
+// them on the diagonal of T's buffer; phase 1 of the next iteration replaces them by their
+// inverses.
+template <int J0>
 __device__ __forceinline__ void tdiag_role(Smem& sm, int l, int64_t nchunks) {
   const int lr = l & 15, lg = l >> 4;
   __syncthreads();
   for (int64_t c = -2; c < nchunks; ++c) {
     {
       const int nb = (int)((c + 1) & 1);
-      f4 rowN[4];
+      f4 rowN[2];
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        const h4 a = lds4(&sm.t[nb][16 * J + lr][16 * J + 4 * lg]);
-        rowN[J] = f4{(float)a[0], (float)a[1], (float)a[2], (float)a[3]};
+      for (int j = 0; j < 2; ++j) {
+        const h4 a = lds4(&sm.t[nb][16 * (J0 + j) + lr][16 * (J0 + j) + 4 * lg]);
+        rowN[j] = f4{(float)a[0], (float)a[1], (float)a[2], (float)a[3]};
       }
-      h4 Tr[4], Tc[4];
-      invert_diag4(rowN, lr, lg, Tr, Tc);
+      h4 Tr[2];
+      invert_diag<2>(rowN, lr, lg, Tr);
 #pragma unroll
-      for (int J = 0; J < 4; ++J) *reinterpret_cast<h4*>(&sm.t[nb][16 * J + lr][16 * J + 4 * lg]) = Tr[J];
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<h4*>(&sm.t[nb][16 * (J0 + j) + lr][16 * (J0 + j) + 4 * lg]) = Tr[j];
     }
     __syncthreads();
     {
-      const int b2 = (int)(c & 1);  // buffer of chunk c + 2
+      const int b2 = (int)(c & 1);  // T buffer of chunk c + 2
       const Gates& g = sm.gt[kbuf(c + 2)];
-      f4 dec[4], acc[4];
+      f4 dec[2], acc[2];
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        dec[J] = g.beta[16 * J + lr] * diag_decay(g, J, lr, lg);
-        acc[J] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 2; ++j) {
+        dec[j] = g.beta[16 * (J0 + j) + lr] * diag_decay(g, J0 + j, lr, lg);
+        acc[j] = f4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        h8 kf[4];
+      for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int J = 0; J < 4; ++J) kf[J] = lds8(&sm.k[kbuf(c + 2)][16 * J + lr][32 * kk + 8 * lg]);
+        for (int j = 0; j < 2; ++j) {
+          const h8 kf = lds8(&sm.k[kbuf(c + 2)][16 * (J0 + j) + lr][32 * kk + 8 * lg]);
+          acc[j] = mfma32(kf, kf, acc[j]);
+        }
 #pragma unroll
-        for (int J = 0; J < 4; ++J) acc[J] = mfma32(kf[J], kf[J], acc[J]);
-      }
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        f4 a = dec[J] * acc[J];
+      for (int j = 0; j < 2; ++j) {
+        f4 a = dec[j] * acc[j];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (4 * lg + e == lr) a[e] = 0.f;  // strictly lower
-        *reinterpret_cast<h4*>(&sm.t[b2][16 * J + lr][16 * J + 4 * lg]) = to_h4(a);
+        *reinterpret_cast<h4*>(&sm.t[b2][16 * (J0 + j) + lr][16 * (J0 + j) + 4 * lg]) = to_h4(a);
       }
     }
     __syncthreads();
   }
 }
 
-// Role: off-diagonal blocks of T for chunk c + 1 (wave 6, phase 2), by block forward
-// substitution down each column, T_ij = T_ii sum_{k=j}^{i-1} (-A_ik) T_kj, in rounds of
-// mutually independent blocks: (1,0) (2,1) (3,2), then (2,0) (3,1), then (3,0).  Phase 1
-// writes the gate tables of chunk c + 2.
-__device__ __forceinline__ void toff_role(Smem& sm, const ChunkArgs& p, int64_t bh, int l, int64_t nchunks) {
+// Off-diagonal blocks of T for chunk c + 1 by block forward substitution down a column,
+// T_ij = T_ii sum_{k=j}^{i-1} (-A_ik) T_kj; lane holds col(T_ij): T[16 i + 4 lg + e][16 j + lr].
+// COLS = 0: column 0 (blocks (1,0), (2,0), (3,0)); COLS = 1: columns 1 and 2.
+template <int COLS>
+__device__ __forceinline__ void toff_part(Smem& sm, int64_t c, int l) {
   const int lr = l & 15, lg = l >> 4;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  const int nb = (int)((c + 1) & 1);
+  auto tr = [&](int i) { return lds4(&sm.t[nb][16 * i + lr][16 * i + 4 * lg]); };
+  auto an = [&](int i, int k) { return lds4(&sm.an[nb][an_idx(i, k)][lr][4 * lg]); };
+  auto put = [&](int i, int j, h4 y) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.t[nb][16 * i + 4 * lg + e][16 * j + lr] = y[e];
+  };
+  if constexpr (COLS == 0) {
+    const h4 tc0 = col_tr(&sm.t[nb][0][0], LC, 0, 0, l);
+    const h4 t1 = tr(1), t2 = tr(2), t3 = tr(3);
+    const h4 a10 = an(1, 0), a20 = an(2, 0), a21 = an(2, 1), a30 = an(3, 0), a31 = an(3, 1), a32 = an(3, 2);
+    const f4 p20 = mfma16(a20, tc0, zero), p30 = mfma16(a30, tc0, zero);
+    const h4 y10 = to_h4(mfma16(t1, to_h4(mfma16(a10, tc0, zero)), zero));
+    const h4 y20 = to_h4(mfma16(t2, to_h4(mfma16(a21, y10, p20)), zero));
+    const h4 y30 = to_h4(mfma16(t3, to_h4(mfma16(a32, y20, mfma16(a31, y10, p30))), zero));
+    put(1, 0, y10); put(2, 0, y20); put(3, 0, y30);
+  } else {
+    const h4 tc1 = col_tr(&sm.t[nb][0][0], LC, 16, 16, l), tc2 = col_tr(&sm.t[nb][0][0], LC, 32, 32, l);
+    const h4 t2 = tr(2), t3 = tr(3);
+    const h4 a21 = an(2, 1), a31 = an(3, 1), a32 = an(3, 2);
+    const f4 p31 = mfma16(a31, tc1, zero);
+    const h4 y21 = to_h4(mfma16(t2, to_h4(mfma16(a21, tc1, zero)), zero));
+    const h4 y32 = to_h4(mfma16(t3, to_h4(mfma16(a32, tc2, zero)), zero));
+    const h4 y31 = to_h4(mfma16(t3, to_h4(mfma16(a32, y21, p31)), zero));
+    put(2, 1, y21); put(3, 2, y32); put(3, 1, y31);
+  }
+}
+
+// Role: keys of chunk c + 2, half `half` (waves 6, 7, phase 1; their buffer was last read in the
+// previous phase 2), and part COLS = half of the off-diagonal blocks of T for chunk c + 1
+// (phase 2).
+template <int half>
+__device__ __forceinline__ void key_toff_role(Smem& sm, const ChunkArgs& p, int64_t bh, int l, int64_t nchunks) {
+  RowStage<half> ks(p.k, p, bh, l);
+  ks.load(0);
+  __syncthreads();
+  for (int64_t c = -2; c < nchunks; ++c) {
+    ks.store(sm.k[kbuf(c + 2)]);
+    ks.load((c + 3) * C);
+    __syncthreads();
+    toff_part<half>(sm, c, l);
+    __syncthreads();
+  }
+}
+
+// Role: gate tables of chunk c + 2 (wave 8, phase 1; their buffer last held chunk c - 1), and the
+// second half of the queries and the value slice of chunk c + 1 (phase 2; every reader of those
+// buffers runs in phase 1).
+__device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int64_t bh, int c0, int l,
+                                              int64_t nchunks) {
   const int64_t tok0 = bh * p.T;
   const auto br = stream_rsrc(p.beta, tok0, p.T);
   const auto gr = stream_rsrc(p.log_alpha, tok0, p.T);
+  const auto vr = stream_rsrc(p.v, tok0 * D, p.T * D);
+  const int dq = l & 3, vq = l >> 2;    // values: channels c0 + 8 dq .., tokens 4 vq .. 4 vq + 3
+  RowStage<1> qs(p.q, p, bh, l);
   uint32_t bb, gg;
+  v4u vv[4];
   auto load_g = [&](int64_t t0) {
     bb = __builtin_amdgcn_raw_buffer_load_b16(br, (int)((t0 + l) * 2), 0, 0);
     gg = __builtin_amdgcn_raw_buffer_load_b16(gr, (int)((t0 + l) * 2), 0, 0);
   };
+  auto load_v = [&](int64_t t0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = ld_b128(vr, (t0 + 4 * vq + e) * D + c0 + 8 * dq);
+  };
   load_g(0);
+  qs.load(-C);
+  load_v(-C);
   __syncthreads();
   for (int64_t c = -2; c < nchunks; ++c) {
-    const int nb = (int)((c + 1) & 1);
-    // gate tables of chunk c + 2 (their buffer last held chunk c - 1)
     {
       const float x = wave_prefix_sum(bf16_bits_to_f32(gg & 0xffffu));
       const float glast = __shfl(x, C - 1, 64);
@@ -471,126 +542,106 @@ __device__ __forceinline__ void toff_role(Smem& sm, const ChunkArgs& p, int64_t 
       const float gref = R == 0 ? 0.f : (R == 1 ? gr1 : (R == 2 ? gr2 : gr3));
       const float beta = bf16_bits_to_f32(bb & 0xffffu);
       Gates& gt = sm.gt[kbuf(c + 2)];
+      const float gam = __expf(x), el = __expf(x - gref);
       gt.G[l] = x;
-      gt.gam[l] = __expf(x);
+      gt.gam[l] = gam;
       gt.dec[l] = __expf(glast - x);
       gt.beta[l] = beta;
-      const float el = __expf(x - gref);
       gt.el[l] = el;
       gt.nbel[l] = -beta * el;
       gt.er[0][l] = __expf(fminf(gr1 - x, 0.f));
       gt.er[1][l] = __expf(fminf(gr2 - x, 0.f));
       gt.er[2][l] = __expf(fminf(gr3 - x, 0.f));
+      gt.bbg[l][0] = (_Float16)beta;
+      gt.bbg[l][1] = (_Float16)(beta * gam);
       load_g((c + 3) * C);
     }
     __syncthreads();
-    h4 Tr[4], Tc[4], an[6];
+    qs.store(sm.q);
+    qs.load((c + 2) * C);
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      Tr[J] = lds4(&sm.t[nb][16 * J + lr][16 * J + 4 * lg]);
-      Tc[J] = col_tr(&sm.t[nb][0][0], LC, 16 * J, 16 * J, l);
+    for (int e = 0; e < 8; ++e) {  // value channel 8 dq + e: tokens 4 vq .. 4 vq + 3 (bf16 bits)
+      uint2 o;
+      o.x = pick2(vv[0][e >> 1], vv[1][e >> 1], e);
+      o.y = pick2(vv[2][e >> 1], vv[3][e >> 1], e);
+      *reinterpret_cast<uint2*>(&sm.vt[8 * dq + e][4 * vq]) = o;
     }
-#pragma unroll
-    for (int i = 0; i < 6; ++i) an[i] = lds4(&sm.an[i][lr][4 * lg]);
-    // lane holds col(T_ij): T[16 i + 4 lg + e][16 j + lr]
-    auto put = [&](int i, int j, h4 y) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.t[nb][16 * i + 4 * lg + e][16 * j + lr] = y[e];
-    };
-    h4 y10, y21, y32, y20, y31, y30;
-    {
-      const h4 z10 = to_h4(mfma16(an[an_idx(1, 0)], Tc[0], zero));
-      const h4 z21 = to_h4(mfma16(an[an_idx(2, 1)], Tc[1], zero));
-      const h4 z32 = to_h4(mfma16(an[an_idx(3, 2)], Tc[2], zero));
-      y10 = to_h4(mfma16(Tr[1], z10, zero));
-      y21 = to_h4(mfma16(Tr[2], z21, zero));
-      y32 = to_h4(mfma16(Tr[3], z32, zero));
-    }
-    {
-      const h4 z20 = to_h4(mfma16(an[an_idx(2, 1)], y10, mfma16(an[an_idx(2, 0)], Tc[0], zero)));
-      const h4 z31 = to_h4(mfma16(an[an_idx(3, 2)], y21, mfma16(an[an_idx(3, 1)], Tc[1], zero)));
-      y20 = to_h4(mfma16(Tr[2], z20, zero));
-      y31 = to_h4(mfma16(Tr[3], z31, zero));
-    }
-    {
-      const f4 z = mfma16(an[an_idx(3, 1)], y10, mfma16(an[an_idx(3, 0)], Tc[0], zero));
-      y30 = to_h4(mfma16(Tr[3], to_h4(mfma16(an[an_idx(3, 2)], y20, z)), zero));
-    }
-    put(1, 0, y10); put(2, 1, y21); put(3, 2, y32); put(2, 0, y20); put(3, 1, y31); put(3, 0, y30);
+    load_v((c + 2) * C);
     __syncthreads();
   }
 }
 
-// Role: keys and P (wave 7).  Phase 1 converts and writes the row-major keys of chunk c + 2
-// (their buffer was last read in the previous phase 2); phase 2 computes
-// P = tril(Q K^T * D) of chunk c + 1, used by the outputs one iteration later.
-__device__ __forceinline__ void pgram_k_role(Smem& sm, const ChunkArgs& p, int64_t bh, int l, int64_t nchunks) {
-  const int lr = l & 15, lg = l >> 4;
-  constexpr int RR[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3}, JJ[10] = {0, 1, 2, 3, 0, 0, 0, 1, 1, 2};
-  const auto kr = stream_rsrc(p.k, bh * p.T * D, p.T * D);
-  const int ch = l & 15, rq = l >> 4;   // 16-byte group ch of rows 4 i + rq
-  v4u rows[16];
-  auto load_rows = [&](int64_t t0) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) rows[i] = ld_b128(kr, (t0 + 4 * i + rq) * D + 8 * ch);
-  };
-  load_rows(0);
+// Role: first half of the queries of chunk c + 1 (wave 9, phase 2).
+__device__ __forceinline__ void q_role(Smem& sm, const ChunkArgs& p, int64_t bh, int l, int64_t nchunks) {
+  RowStage<0> qs(p.q, p, bh, l);
+  qs.load(-C);
   __syncthreads();
   for (int64_t c = -2; c < nchunks; ++c) {
-    {
-      const int b = kbuf(c + 2);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) *reinterpret_cast<h8*>(&sm.k[b][4 * i + rq][8 * ch]) = bf8_to_h8(rows[i]);
-      load_rows((c + 3) * C);
-    }
     __syncthreads();
-    const int nb = (int)((c + 1) & 1);
-    const Gates& g = sm.gt[kbuf(c + 1)];
-    f4 acc[10];
-#pragma unroll
-    for (int t = 0; t < 10; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      h8 kf[4], qf[4];
-#pragma unroll
-      for (int J = 0; J < 4; ++J) kf[J] = lds8(&sm.k[kbuf(c + 1)][16 * J + lr][32 * kk + 8 * lg]);
-#pragma unroll
-      for (int R = 0; R < 4; ++R) qf[R] = lds8(&sm.q[nb][16 * R + lr][32 * kk + 8 * lg]);
-#pragma unroll
-      for (int t = 0; t < 10; ++t) acc[t] = mfma32(kf[JJ[t]], qf[RR[t]], acc[t]);
-    }
-#pragma unroll
-    for (int J = 0; J < 4; ++J)
-      *reinterpret_cast<h4*>(&sm.p[nb][16 * J + lr][16 * J + 4 * lg]) = to_h4(diag_decay(g, J, lr, lg) * acc[J]);
-#pragma unroll
-    for (int t = 4; t < 10; ++t)
-      *reinterpret_cast<h4*>(&sm.p[nb][16 * RR[t] + lr][16 * JJ[t] + 4 * lg]) = to_h4(offdiag_p(g, RR[t], JJ[t], lr, lg, acc[t]));
+    qs.store(sm.q);
+    qs.load((c + 2) * C);
     __syncthreads();
   }
 }
 
-// Role: off-diagonal A (wave 3, phase 1): the off-diagonal blocks of -A of chunk c + 1.
-__device__ __forceinline__ void aoff_role(Smem& sm, int l, int64_t nchunks) {
+// Role: half SET of the tiles of P = tril(Q K^T * D) of chunk c (waves 10, 11, phase 1; read by
+// the outputs in phase 2), and half SET of the off-diagonal blocks of -A of chunk c + 2
+// (phase 2; their keys and gates were staged in phase 1), used one iteration later.
+template <int SET>
+__device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
   const int lr = l & 15, lg = l >> 4;
-  constexpr int RR[6] = {1, 2, 3, 2, 3, 3}, JJ[6] = {0, 0, 0, 1, 1, 2};
+  // P tiles (R, J): set 0 = (0,0) (1,1) (1,0) (2,0) (3,0); set 1 = (2,2) (3,3) (2,1) (3,1) (3,2).
+  constexpr int PR[2][5] = {{0, 1, 1, 2, 3}, {2, 3, 2, 3, 3}}, PJ[2][5] = {{0, 1, 0, 0, 0}, {2, 3, 1, 1, 2}};
+  // A tiles: set 0 = (1,0) (2,0) (3,0); set 1 = (2,1) (3,1) (3,2).
+  constexpr int AR[2][3] = {{1, 2, 3}, {2, 3, 3}}, AJ[2][3] = {{0, 0, 0}, {1, 1, 2}};
+  constexpr int J0 = SET == 0 ? 0 : 1, J1 = SET == 0 ? 1 : 3;   // key blocks of P's tiles
+  constexpr int R0 = SET == 0 ? 0 : 2;                           // query blocks R0..3
   __syncthreads();
   for (int64_t c = -2; c < nchunks; ++c) {
-    const Gates& g = sm.gt[kbuf(c + 1)];
-    f4 acc[6];
+    {
+      const Gates& g = sm.gt[kbuf(c)];
+      f4 acc[5];
 #pragma unroll
-    for (int t = 0; t < 6; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 5; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      h8 kf[4];
+      for (int kk = 0; kk < 4; ++kk) {
+        h8 kf[4], qf[4];
 #pragma unroll
-      for (int J = 0; J < 4; ++J) kf[J] = lds8(&sm.k[kbuf(c + 1)][16 * J + lr][32 * kk + 8 * lg]);
+        for (int J = J0; J <= J1; ++J) kf[J] = lds8(&sm.k[kbuf(c)][16 * J + lr][32 * kk + 8 * lg]);
 #pragma unroll
-      for (int t = 0; t < 6; ++t) acc[t] = mfma32(kf[JJ[t]], kf[RR[t]], acc[t]);
+        for (int R = R0; R < 4; ++R) qf[R] = lds8(&sm.q[16 * R + lr][32 * kk + 8 * lg]);
+#pragma unroll
+        for (int t = 0; t < 5; ++t) acc[t] = mfma32(kf[PJ[SET][t]], qf[PR[SET][t]], acc[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        *reinterpret_cast<h4*>(&sm.p[16 * PR[SET][t] + lr][16 * PJ[SET][t] + 4 * lg]) =
+            to_h4(diag_decay(g, PR[SET][t], lr, lg) * acc[t]);
+#pragma unroll
+      for (int t = 2; t < 5; ++t)
+        *reinterpret_cast<h4*>(&sm.p[16 * PR[SET][t] + lr][16 * PJ[SET][t] + 4 * lg]) =
+            to_h4(offdiag_p(g, PR[SET][t], PJ[SET][t], lr, lg, acc[t]));
     }
-#pragma unroll
-    for (int t = 0; t < 6; ++t)
-      *reinterpret_cast<h4*>(&sm.an[an_idx(RR[t], JJ[t])][lr][4 * lg]) = to_h4(offdiag_neg_a(g, RR[t], JJ[t], lr, lg, acc[t]));
     __syncthreads();
+    {
+      const int kb2 = kbuf(c + 2), ab = (int)(c & 1);
+      const Gates& g = sm.gt[kb2];
+      f4 acc[3];
+#pragma unroll
+      for (int t = 0; t < 3; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        h8 kf[4];
+#pragma unroll
+        for (int J = SET; J < 4; ++J) kf[J] = lds8(&sm.k[kb2][16 * J + lr][32 * kk + 8 * lg]);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) acc[t] = mfma32(kf[AJ[SET][t]], kf[AR[SET][t]], acc[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        *reinterpret_cast<h4*>(&sm.an[ab][an_idx(AR[SET][t], AJ[SET][t])][lr][4 * lg]) =
+            to_h4(offdiag_neg_a(g, AR[SET][t], AJ[SET][t], lr, lg, acc[t]));
+    }
     __syncthreads();
   }
 }
@@ -613,22 +664,27 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
 
   // T and P start at zero; their upper blocks are never written
   for (int e = tid; e < 2 * C * LC / 8; e += NTH) reinterpret_cast<v4u*>(&sm.t[0][0][0])[e] = v4u{0u, 0u, 0u, 0u};
-  for (int e = tid; e < 2 * C * LC / 8; e += NTH) reinterpret_cast<v4u*>(&sm.p[0][0][0])[e] = v4u{0u, 0u, 0u, 0u};
+  for (int e = tid; e < C * LC / 8; e += NTH) reinterpret_cast<v4u*>(&sm.p[0][0])[e] = v4u{0u, 0u, 0u, 0u};
 
-  // Every role runs nchunks + 2 iterations of two barriers after one initial barrier.  Waves w
-  // and w + 4 share a SIMD: the chains (0, 1) share theirs with the outputs (4, 5).
+  // Every role runs nchunks + 2 iterations of two barriers after one initial barrier.  Waves w,
+  // w + 4 and w + 8 share a SIMD: each chain (0, 1) shares its SIMD with an output wave (4, 5)
+  // and a staging wave (8, 9); the producers (2, 3, 6, 7, 10, 11) fill the other two SIMDs.
   switch (w) {
     case 0:
     case 1:
       __builtin_amdgcn_s_setprio(2);
       chain_role(sm, p, bh, c0, w, l, nchunks);
       break;
-    case 2: tdiag_role(sm, l, nchunks); break;
-    case 3: aoff_role(sm, l, nchunks); break;
+    case 2: tdiag_role<0>(sm, l, nchunks); break;
+    case 3: tdiag_role<2>(sm, l, nchunks); break;
     case 4: out_role<TOut, 0>(sm, p, bh, c0, l, nchunks); break;
     case 5: out_role<TOut, 2>(sm, p, bh, c0, l, nchunks); break;
-    case 6: toff_role(sm, p, bh, l, nchunks); break;
-    default: pgram_k_role(sm, p, bh, l, nchunks); break;
+    case 6: key_toff_role<0>(sm, p, bh, l, nchunks); break;
+    case 7: key_toff_role<1>(sm, p, bh, l, nchunks); break;
+    case 8: gates_qv_role(sm, p, bh, c0, l, nchunks); break;
+    case 9: q_role(sm, p, bh, l, nchunks); break;
+    case 10: pa_role<0>(sm, l, nchunks); break;
+    default: pa_role<1>(sm, l, nchunks); break;
   }
 }
 
