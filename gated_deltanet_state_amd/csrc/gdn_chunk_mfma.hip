@@ -86,7 +86,7 @@ struct alignas(16) Smem {
   alignas(16) Gates gt[3];
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
-__device__ __forceinline__ int kbuf(int64_t chunk) { return (int)(((chunk % 3) + 3) % 3); }
+__device__ __forceinline__ int kbuf(int chunk) { return (chunk + 3) % 3; }  // chunk >= -3
 
 constexpr int an_idx(int R, int J) { return R * (R - 1) / 2 + J; }
 
@@ -98,6 +98,11 @@ __device__ __forceinline__ v4u ld_b128(__amdgpu_buffer_rsrc_t r, int64_t elem) {
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 __device__ __forceinline__ h8 lds8(const _Float16* p) { return *reinterpret_cast<const h8*>(p); }
+// Keeps the scheduler from moving instructions across this point: fragment loads for the next
+// contraction step are issued before the MFMAs of the current one and no earlier, so at most
+// two steps of loads are in flight and each wait names only the step it needs (the LDS counter
+// tracks at most 15 outstanding operations).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ __forceinline__ h4 lds4(const _Float16* p) { return *reinterpret_cast<const h4*>(p); }
 
 // Dword m of the 16-bit transpose: halves e of dwords x (low result half) and y (high).
@@ -221,7 +226,7 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
   }
   __syncthreads();
 
-  for (int64_t c = -2; c < nchunks; ++c) {
+  for (int c = -2; c < (int)nchunks; ++c) {
     h8 Ub[2], kt0[8];
     if (c >= 0) {
       const int kb3 = kbuf(c);
@@ -233,15 +238,29 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
         bg[i] = lds8(&g.bbg[16 * i + 4 * lg][0]);
         vv[i] = *reinterpret_cast<const uint2*>(&sm.vt[dv][16 * i + 4 * lg]);
       }
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) kt0[kb] = lds8(&sm.kt[16 * kb + lr][8 * lg]);
       f4 X[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) X[i] = f4{0.f, 0.f, 0.f, 0.f};
+      h8 kfr[2][4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int i = 0; i < 4; ++i) kfr[0][i] = lds8(&sm.k[kb3][16 * i + lr][8 * lg]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[i] = mfma32(lds8(&sm.k[kb3][16 * i + lr][32 * kk + 8 * lg]), Sb[kk], X[i]);
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kfr[(kk + 1) & 1][i] = lds8(&sm.k[kb3][16 * i + lr][32 * (kk + 1) + 8 * lg]);
+        }
+        sched_fence();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[i] = mfma32(kfr[kk & 1][i], Sb[kk], X[i]);
+        sched_fence();
+      }
+      h8 tf[6];
+#pragma unroll
+      for (int i = 0, m = 0; i < 4; ++i) {
+        tf[m++] = lds8(&sm.t[(int)(c & 1)][16 * i + lr][8 * lg]);
+        if (i >= 2) tf[m++] = lds8(&sm.t[(int)(c & 1)][16 * i + lr][32 + 8 * lg]);
+      }
       // lane: tokens 16 i + 4 lg + e, value channel dv; X = beta v - beta gamma (K S^T)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -253,21 +272,23 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
       const h8 Xb0 = pair_k32(to_h4(X[0]), to_h4(X[1])), Xb1 = pair_k32(to_h4(X[2]), to_h4(X[3]));
       f4 U[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        U[i] = mfma32(lds8(&sm.t[(int)(c & 1)][16 * i + lr][8 * lg]), Xb0, f4{0.f, 0.f, 0.f, 0.f});
-        if (i >= 2) U[i] = mfma32(lds8(&sm.t[(int)(c & 1)][16 * i + lr][32 + 8 * lg]), Xb1, U[i]);
+      for (int i = 0, m = 0; i < 4; ++i) {
+        U[i] = mfma32(tf[m++], Xb0, f4{0.f, 0.f, 0.f, 0.f});
+        if (i >= 2) U[i] = mfma32(tf[m++], Xb1, U[i]);
       }
       Ub[0] = pair_k32(to_h4(U[0]), to_h4(U[1]));
       Ub[1] = pair_k32(to_h4(U[2]), to_h4(U[3]));
       *reinterpret_cast<h8*>(&sm.u[dv][8 * lg]) = Ub[0];
       *reinterpret_cast<h8*>(&sm.u[dv][32 + 8 * lg]) = Ub[1];
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) kt0[kb] = lds8(&sm.kt[16 * kb + lr][8 * lg]);
       const float gC = g.gam[C - 1];
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) St[kb] *= gC;
     }
     __syncthreads();
     if (c >= 0) {
-      const int64_t t0 = c * C;
+      const int64_t t0 = (int64_t)c * C;
       const int n = (int)(T - t0 < C ? T - t0 : C);
       h8 kt1[8];
 #pragma unroll
@@ -351,22 +372,30 @@ __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, int64_t b
   const auto orr = __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<TOut*>(p.o) + tok0 * D), 0,
                                                      (int)(T * D * (int64_t)sizeof(TOut)), kRsrcWord3);
   __syncthreads();
-  for (int64_t c = -2; c < nchunks; ++c) {
+  for (int c = -2; c < (int)nchunks; ++c) {
     f4 Oa[2][2];
     // ---- phase 1: O = diag(gamma) Q S^T for chunk c
 #pragma unroll
     for (int t = 0; t < 2; ++t) Oa[t][0] = Oa[t][1] = f4{0.f, 0.f, 0.f, 0.f};
+    {
+      h8 fr[2][4];  // [step parity][q0 q1 s0 s1]
+      auto ld = [&](int kk, h8 (&f)[4]) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      h8 qf[2], sf[2];
+        for (int t = 0; t < 2; ++t) f[t] = lds8(&sm.q[16 * (tb0 + t) + lr][32 * kk + 8 * lg]);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) qf[t] = lds8(&sm.q[16 * (tb0 + t) + lr][32 * kk + 8 * lg]);
+        for (int d = 0; d < 2; ++d) f[2 + d] = lds8(&sm.s[16 * d + lr][32 * kk + 8 * lg]);
+      };
+      ld(0, fr[0]);
 #pragma unroll
-      for (int d = 0; d < 2; ++d) sf[d] = lds8(&sm.s[16 * d + lr][32 * kk + 8 * lg]);
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) ld(kk + 1, fr[(kk + 1) & 1]);
+        sched_fence();
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int d = 0; d < 2; ++d) Oa[t][d] = mfma32(sf[d], qf[t], Oa[t][d]);
+          for (int d = 0; d < 2; ++d) Oa[t][d] = mfma32(fr[kk & 1][2 + d], fr[kk & 1][t], Oa[t][d]);
+        sched_fence();
+      }
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -377,7 +406,7 @@ __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, int64_t b
     stage_kt(sm, &sm.k[kbuf(c)][0][0], sm.gt[kbuf(c)], 2 * tb0, 1, l);
     __syncthreads();
     // ---- phase 2: O += P U, write o; transposed keys (tokens 0..31) of chunk c + 1
-    const int64_t t0 = c * C;
+    const int64_t t0 = (int64_t)c * C;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int tb = tb0 + t;
@@ -412,7 +441,7 @@ template <int J0>
 __device__ __forceinline__ void tdiag_role(Smem& sm, int l, int64_t nchunks) {
   const int lr = l & 15, lg = l >> 4;
   __syncthreads();
-  for (int64_t c = -2; c < nchunks; ++c) {
+  for (int c = -2; c < (int)nchunks; ++c) {
     {
       const int nb = (int)((c + 1) & 1);
       f4 rowN[2];
@@ -496,15 +525,21 @@ __device__ __forceinline__ void toff_part(Smem& sm, int64_t c, int l) {
 // (phase 2).
 template <int half>
 __device__ __forceinline__ void key_toff_role(Smem& sm, const ChunkArgs& p, int64_t bh, int l, int64_t nchunks) {
-  RowStage<half> ks(p.k, p, bh, l);
-  ks.load(0);
-  __syncthreads();
-  for (int64_t c = -2; c < nchunks; ++c) {
+  // two register sets: each chunk's rows are loaded two iterations before they are stored
+  RowStage<half> ka(p.k, p, bh, l), kb(p.k, p, bh, l);
+  ka.load(0);
+  kb.load(C);
+  auto iter = [&](int c, RowStage<half>& ks) {
     ks.store(sm.k[kbuf(c + 2)]);
-    ks.load((c + 3) * C);
+    ks.load((int64_t)(c + 4) * C);
     __syncthreads();
     toff_part<half>(sm, c, l);
     __syncthreads();
+  };
+  __syncthreads();
+  for (int c = -2; c < (int)nchunks; c += 2) {
+    iter(c, ka);
+    if (c + 1 < (int)nchunks) iter(c + 1, kb);
   }
 }
 
@@ -518,29 +553,36 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int6
   const auto gr = stream_rsrc(p.log_alpha, tok0, p.T);
   const auto vr = stream_rsrc(p.v, tok0 * D, p.T * D);
   const int dq = l & 3, vq = l >> 2;    // values: channels c0 + 8 dq .., tokens 4 vq .. 4 vq + 3
-  RowStage<1> qs(p.q, p, bh, l);
-  uint32_t bb, gg;
-  v4u vv[4];
-  auto load_g = [&](int64_t t0) {
-    bb = __builtin_amdgcn_raw_buffer_load_b16(br, (int)((t0 + l) * 2), 0, 0);
-    gg = __builtin_amdgcn_raw_buffer_load_b16(gr, (int)((t0 + l) * 2), 0, 0);
+  struct Set {
+    uint32_t bb, gg;
+    v4u vv[4];
   };
-  auto load_v = [&](int64_t t0) {
+  RowStage<1> qa(p.q, p, bh, l), qb(p.q, p, bh, l);
+  Set sa, sb;
+  auto load_g = [&](Set& st, int64_t t0) {
+    st.bb = __builtin_amdgcn_raw_buffer_load_b16(br, (int)((t0 + l) * 2), 0, 0);
+    st.gg = __builtin_amdgcn_raw_buffer_load_b16(gr, (int)((t0 + l) * 2), 0, 0);
+  };
+  auto load_v = [&](Set& st, int64_t t0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vv[e] = ld_b128(vr, (t0 + 4 * vq + e) * D + c0 + 8 * dq);
+    for (int e = 0; e < 4; ++e) st.vv[e] = ld_b128(vr, (t0 + 4 * vq + e) * D + c0 + 8 * dq);
   };
-  load_g(0);
-  qs.load(-C);
-  load_v(-C);
-  __syncthreads();
-  for (int64_t c = -2; c < nchunks; ++c) {
+  // two register sets: gates of chunk c + 2 and queries/values of chunk c + 1 are loaded two
+  // iterations before they are stored
+  load_g(sa, 0);
+  load_g(sb, C);
+  qa.load(-C);
+  load_v(sa, -C);
+  qb.load(0);
+  load_v(sb, 0);
+  auto iter = [&](int c, Set& st, RowStage<1>& qs) {
     {
-      const float x = wave_prefix_sum(bf16_bits_to_f32(gg & 0xffffu));
+      const float x = wave_prefix_sum(bf16_bits_to_f32(st.gg & 0xffffu));
       const float glast = __shfl(x, C - 1, 64);
       const float gr1 = __shfl(x, 15, 64), gr2 = __shfl(x, 31, 64), gr3 = __shfl(x, 47, 64);
       const int R = l >> 4;
       const float gref = R == 0 ? 0.f : (R == 1 ? gr1 : (R == 2 ? gr2 : gr3));
-      const float beta = bf16_bits_to_f32(bb & 0xffffu);
+      const float beta = bf16_bits_to_f32(st.bb & 0xffffu);
       Gates& gt = sm.gt[kbuf(c + 2)];
       const float gam = __expf(x), el = __expf(x - gref);
       gt.G[l] = x;
@@ -554,33 +596,43 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int6
       gt.er[2][l] = __expf(fminf(gr3 - x, 0.f));
       gt.bbg[l][0] = (_Float16)beta;
       gt.bbg[l][1] = (_Float16)(beta * gam);
-      load_g((c + 3) * C);
+      load_g(st, (int64_t)(c + 4) * C);
     }
     __syncthreads();
     qs.store(sm.q);
-    qs.load((c + 2) * C);
+    qs.load((int64_t)(c + 3) * C);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {  // value channel 8 dq + e: tokens 4 vq .. 4 vq + 3 (bf16 bits)
       uint2 o;
-      o.x = pick2(vv[0][e >> 1], vv[1][e >> 1], e);
-      o.y = pick2(vv[2][e >> 1], vv[3][e >> 1], e);
+      o.x = pick2(st.vv[0][e >> 1], st.vv[1][e >> 1], e);
+      o.y = pick2(st.vv[2][e >> 1], st.vv[3][e >> 1], e);
       *reinterpret_cast<uint2*>(&sm.vt[8 * dq + e][4 * vq]) = o;
     }
-    load_v((c + 2) * C);
+    load_v(st, (int64_t)(c + 3) * C);
     __syncthreads();
+  };
+  __syncthreads();
+  for (int c = -2; c < (int)nchunks; c += 2) {
+    iter(c, sa, qa);
+    if (c + 1 < (int)nchunks) iter(c + 1, sb, qb);
   }
 }
 
-// Role: first half of the queries of chunk c + 1 (wave 9, phase 2).
+// Role: first half of the queries of chunk c + 1 (wave 9, phase 2), loaded two iterations ahead.
 __device__ __forceinline__ void q_role(Smem& sm, const ChunkArgs& p, int64_t bh, int l, int64_t nchunks) {
-  RowStage<0> qs(p.q, p, bh, l);
-  qs.load(-C);
-  __syncthreads();
-  for (int64_t c = -2; c < nchunks; ++c) {
+  RowStage<0> qa(p.q, p, bh, l), qb(p.q, p, bh, l);
+  qa.load(-C);
+  qb.load(0);
+  auto iter = [&](int c, RowStage<0>& qs) {
     __syncthreads();
     qs.store(sm.q);
-    qs.load((c + 2) * C);
+    qs.load((int64_t)(c + 3) * C);
     __syncthreads();
+  };
+  __syncthreads();
+  for (int c = -2; c < (int)nchunks; c += 2) {
+    iter(c, qa);
+    if (c + 1 < (int)nchunks) iter(c + 1, qb);
   }
 }
 
@@ -597,50 +649,67 @@ __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
   constexpr int J0 = SET == 0 ? 0 : 1, J1 = SET == 0 ? 1 : 3;   // key blocks of P's tiles
   constexpr int R0 = SET == 0 ? 0 : 2;                           // query blocks R0..3
   __syncthreads();
-  for (int64_t c = -2; c < nchunks; ++c) {
+  for (int c = -2; c < (int)nchunks; ++c) {
     {
       const Gates& g = sm.gt[kbuf(c)];
-      f4 acc[5];
+      f4 fac[5], acc[5];  // decay factors first: their reads and exponentials overlap the MFMAs
+#pragma unroll
+      for (int t = 0; t < 2; ++t) fac[t] = diag_decay(g, PR[SET][t], lr, lg);
+#pragma unroll
+      for (int t = 2; t < 5; ++t) fac[t] = offdiag_p(g, PR[SET][t], PJ[SET][t], lr, lg, f4{1.f, 1.f, 1.f, 1.f});
 #pragma unroll
       for (int t = 0; t < 5; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+      {
+        h8 kf[2][4], qf[2][4];
+        auto ld = [&](int kk, h8 (&k4)[4], h8 (&q4)[4]) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        h8 kf[4], qf[4];
+          for (int J = J0; J <= J1; ++J) k4[J] = lds8(&sm.k[kbuf(c)][16 * J + lr][32 * kk + 8 * lg]);
 #pragma unroll
-        for (int J = J0; J <= J1; ++J) kf[J] = lds8(&sm.k[kbuf(c)][16 * J + lr][32 * kk + 8 * lg]);
+          for (int R = R0; R < 4; ++R) q4[R] = lds8(&sm.q[16 * R + lr][32 * kk + 8 * lg]);
+        };
+        ld(0, kf[0], qf[0]);
 #pragma unroll
-        for (int R = R0; R < 4; ++R) qf[R] = lds8(&sm.q[16 * R + lr][32 * kk + 8 * lg]);
+        for (int kk = 0; kk < 4; ++kk) {
+          if (kk < 3) ld(kk + 1, kf[(kk + 1) & 1], qf[(kk + 1) & 1]);
+          sched_fence();
 #pragma unroll
-        for (int t = 0; t < 5; ++t) acc[t] = mfma32(kf[PJ[SET][t]], qf[PR[SET][t]], acc[t]);
+          for (int t = 0; t < 5; ++t) acc[t] = mfma32(kf[kk & 1][PJ[SET][t]], qf[kk & 1][PR[SET][t]], acc[t]);
+          sched_fence();
+        }
       }
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        *reinterpret_cast<h4*>(&sm.p[16 * PR[SET][t] + lr][16 * PJ[SET][t] + 4 * lg]) =
-            to_h4(diag_decay(g, PR[SET][t], lr, lg) * acc[t]);
-#pragma unroll
-      for (int t = 2; t < 5; ++t)
-        *reinterpret_cast<h4*>(&sm.p[16 * PR[SET][t] + lr][16 * PJ[SET][t] + 4 * lg]) =
-            to_h4(offdiag_p(g, PR[SET][t], PJ[SET][t], lr, lg, acc[t]));
+      for (int t = 0; t < 5; ++t)
+        *reinterpret_cast<h4*>(&sm.p[16 * PR[SET][t] + lr][16 * PJ[SET][t] + 4 * lg]) = to_h4(fac[t] * acc[t]);
     }
     __syncthreads();
     {
       const int kb2 = kbuf(c + 2), ab = (int)(c & 1);
       const Gates& g = sm.gt[kb2];
-      f4 acc[3];
+      f4 fac[3], acc[3];
 #pragma unroll
-      for (int t = 0; t < 3; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 3; ++t) {
+        fac[t] = offdiag_neg_a(g, AR[SET][t], AJ[SET][t], lr, lg, f4{1.f, 1.f, 1.f, 1.f});
+        acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+      }
+      {
+        h8 kf[2][4];
+        auto ld = [&](int kk, h8 (&k4)[4]) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        h8 kf[4];
+          for (int J = SET; J < 4; ++J) k4[J] = lds8(&sm.k[kb2][16 * J + lr][32 * kk + 8 * lg]);
+        };
+        ld(0, kf[0]);
 #pragma unroll
-        for (int J = SET; J < 4; ++J) kf[J] = lds8(&sm.k[kb2][16 * J + lr][32 * kk + 8 * lg]);
+        for (int kk = 0; kk < 4; ++kk) {
+          if (kk < 3) ld(kk + 1, kf[(kk + 1) & 1]);
+          sched_fence();
 #pragma unroll
-        for (int t = 0; t < 3; ++t) acc[t] = mfma32(kf[AJ[SET][t]], kf[AR[SET][t]], acc[t]);
+          for (int t = 0; t < 3; ++t) acc[t] = mfma32(kf[kk & 1][AJ[SET][t]], kf[kk & 1][AR[SET][t]], acc[t]);
+          sched_fence();
+        }
       }
 #pragma unroll
       for (int t = 0; t < 3; ++t)
-        *reinterpret_cast<h4*>(&sm.an[ab][an_idx(AR[SET][t], AJ[SET][t])][lr][4 * lg]) =
-            to_h4(offdiag_neg_a(g, AR[SET][t], AJ[SET][t], lr, lg, acc[t]));
+        *reinterpret_cast<h4*>(&sm.an[ab][an_idx(AR[SET][t], AJ[SET][t])][lr][4 * lg]) = to_h4(fac[t] * acc[t]);
     }
     __syncthreads();
   }
