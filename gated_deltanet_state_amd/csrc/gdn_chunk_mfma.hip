@@ -17,18 +17,19 @@
 // Work decomposition: a workgroup owns one (batch, head) stream and a 32-row slice of the
 // value channels (the recurrence multiplies S only from the right, so value rows evolve
 // independently); the four slices of a stream are placed on the same XCD so they share its
-// L2.  Eight wavefronts take fixed roles (waves w and w + 4 share a SIMD):
-//   0, 1  state chain: each keeps a 16 x 128 block of S in fp32 MFMA accumulators for the
-//         whole sequence and runs X, U = T X and the state update with every operand
-//         regrouped in registers (no LDS round trip on the chunk-to-chunk dependency);
-//   4, 5  outputs of two 16-token blocks each: O = diag(gamma) Q S^T + P U;
-//   6, 7  one chunk ahead: the diagonal 16x16 blocks of A, their inverses and the
-//         off-diagonal blocks of T (wave 6); the off-diagonal blocks of A (wave 7); the
-//         causal scores P = tril(Q K^T * D) (both);
-//   2, 3  staging: keys (row-major, and transposed for the state update), queries, values
-//         and the gate tables, converted to fp16 and written to LDS one or two chunks ahead.
-// Each iteration has two barrier-separated phases; iteration c works on chunk c (chain,
-// outputs), chunk c + 1 (producers) and chunks c + 1, c + 2 (staging).
+// L2.  Twelve wavefronts take fixed roles (waves w, w + 4 and w + 8 share a SIMD):
+//   0, 1    state chain: each keeps a 16 x 128 block of S in fp32 MFMA accumulators for the
+//           whole sequence and runs X, U = T X and the state update with every operand
+//           regrouped in registers (no LDS round trip on the chunk-to-chunk dependency);
+//   4, 5    outputs of two 16-token blocks each, O = diag(gamma) Q S^T + P U, and the keys
+//           scaled by e^{G_63 - G} and transposed, the A operand of the state update;
+//   10, 11  the causal scores P = tril(Q K^T * D) of the chain's chunk, and the off-diagonal
+//           blocks of A two chunks ahead;
+//   2, 3    the diagonal 16x16 blocks of A two chunks ahead, and their inverses one ahead;
+//   6, 7    keys (fp16, row-major) two chunks ahead, and the off-diagonal blocks of T one ahead;
+//   8, 9    gate tables two chunks ahead; queries and the value slice one ahead.
+// Each iteration has two barrier-separated phases; the staging waves load from HBM two
+// iterations before they store, so global latency never reaches a barrier.
 // The products run on v_mfma_f32_16x16x32_f16 / 16x16x16_f16 with fp32 accumulation.
 // bf16 inputs convert exactly to fp16 (|x| <= 65504); derived operands (S, P, U, T) are
 // rounded to fp16, whose 11-bit significand keeps the bf16-output error budget.
@@ -68,11 +69,19 @@ struct alignas(16) Gates {
 };
 
 // Buffers hold data of one chunk: keys and gate tables by chunk mod 3, T by chunk mod 2, the
-// others single.  Bank layout (gfx950 LDS: 16-byte accesses are served 32 lanes at a time over
-// 128 four-byte banks): a 16-row x 32-column fragment read is conflict-free when the row stride
-// is an odd multiple of 8 banks, hence the 288-byte rows of the [token][channel] tiles and the
-// 160-byte rows of the transposed keys.
-constexpr int LK = C + 16;   // row stride (halves) of the transposed keys
+// others single.  Bank layout, as measured on gfx950 with the LDS bank-conflict counter for
+// 16-row tiles (lane l on row l%16, 16-byte column chunk l/16): fragment reads are
+// conflict-free when the row stride is an odd multiple of 8 four-byte banks, 16-byte writes,
+// 8-byte reads and 2-byte writes when it is an odd multiple of 4.  Tiles that are written in
+// 16-byte rows and read as fragments (the [token][channel] tiles, the transposed keys, U and P)
+// take a stride of the first kind and store the 16-byte chunk c of row r at chunk
+// c ^ ((r >> 2) & 1), which makes both conflict-free.  Their rows are always 16 i + l%16 (or
+// 4 i + l/16 in the staging stores), so the swizzle costs nothing: it is a per-lane constant.
+constexpr int LK = C + 16;   // row stride (halves) of the transposed keys, U and P: 160 bytes = 40 banks
+// Swizzled 16-byte chunk l/16 of rows 16 i + l%16, and the same for the 8-byte column groups
+// (4 elements) of a 16x16 tile.
+__device__ __forceinline__ int swl(int l) { return (l >> 4) ^ ((l >> 2) & 1); }
+__device__ __forceinline__ int swl4(int l) { return (l >> 4) ^ (((l >> 2) & 1) << 1); }
 struct alignas(16) Smem {
   alignas(16) _Float16 k[3][C][LQ];      // keys                                  [token][d_k]
   alignas(16) _Float16 q[C][LQ];         // queries                               [token][d_k]
@@ -80,9 +89,9 @@ struct alignas(16) Smem {
   alignas(16) _Float16 kt[D][LK];        // keys scaled by e^{G_63 - G}, transposed [d_k][token]
   alignas(16) uint16_t vt[DVT][LC];      // value slice, bf16 bits                [d_v][token]
   alignas(16) _Float16 t[2][C][LC];      // T = (I + A)^{-1}, upper blocks zero; A_JJ staged on the diagonal
-  alignas(16) _Float16 p[C][LC];         // tril(Q K^T * D), upper blocks zero     [token][token]
+  alignas(16) _Float16 p[C][LK];         // tril(Q K^T * D), upper blocks zero     [token][token]
   alignas(16) _Float16 an[2][6][16][LT]; // -A, off-diagonal blocks (R, J), R > J, by chunk mod 2
-  alignas(16) _Float16 u[DVT][LC];       // U of the chain's chunk                [d_v][token]
+  alignas(16) _Float16 u[DVT][LK];       // U of the chain's chunk                [d_v][token]
   alignas(16) Gates gt[3];
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
@@ -180,14 +189,17 @@ __device__ __forceinline__ void invert_diag(const f4 (&rowN)[NB], int lr, int lg
 // element (i mod 4) of the 8 bytes addressed by lane (i/4 + 4j), j = 0..3.  frag8_tr builds,
 // from a row-major fp16 matrix M[k][m], the fragment in which lane l holds
 // M[k0 + 8 (l/16) + e][m0 + l%16], e = 0..7: lane s of a group supplies the addresses of 4
-// consecutive columns in rows k0 + 8 (l/16) + s/4 (+4).
+// consecutive columns in rows k0 + 8 (l/16) + s/4 (+4) of a chunk-swizzled tile (k0 a
+// multiple of 32, m0 of 16).
 typedef short s4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ v4u frag8_tr(const _Float16* base, int ld, int k0, int m0, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const _Float16* a = base + (k0 + 8 * lg + (lr >> 2)) * ld + m0 + 4 * (lr & 3);
   typedef unsigned u2 __attribute__((ext_vector_type(2)));
   const u2 x = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(a)));
-  const u2 y = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(a + 4 * ld)));
+  // rows k0 + 8 (l/16) + 4 + s/4 have bit 2 set: their 16-byte chunks are swapped in pairs
+  const _Float16* b = base + (k0 + 8 * lg + (lr >> 2) + 4) * ld + m0 + ((4 * (lr & 3)) ^ 8);
+  const u2 y = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(b)));
   return v4u{x[0], x[1], y[0], y[1]};
 }
 // One transpose read: the accumulator (column) layout of the 16x16 block at (r0, c0) of a
@@ -209,7 +221,7 @@ __device__ __forceinline__ h4 col_tr(const _Float16* base, int ld, int r0, int c
 // other phase-1 operands) and tokens 32..63 in phase 1 (fetched at the start of phase 2).
 __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t bh, int c0, int db, int l,
                                            int64_t nchunks) {
-  const int lr = l & 15, lg = l >> 4, dv = 16 * db + lr;
+  const int lr = l & 15, lg = l >> 4, dv = 16 * db + lr, sg = swl(l);
   const int64_t T = p.T;
   f4 St[8];
 #pragma unroll
@@ -222,7 +234,7 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     Sb[kk] = pair_k32(to_h4(St[2 * kk]), to_h4(St[2 * kk + 1]));
-    *reinterpret_cast<h8*>(&sm.s[dv][32 * kk + 8 * lg]) = Sb[kk];
+    *reinterpret_cast<h8*>(&sm.s[dv][32 * kk + 8 * sg]) = Sb[kk];
   }
   __syncthreads();
 
@@ -243,12 +255,12 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
       for (int i = 0; i < 4; ++i) X[i] = f4{0.f, 0.f, 0.f, 0.f};
       h8 kfr[2][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kfr[0][i] = lds8(&sm.k[kb3][16 * i + lr][8 * lg]);
+      for (int i = 0; i < 4; ++i) kfr[0][i] = lds8(&sm.k[kb3][16 * i + lr][8 * sg]);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         if (kk < 3) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) kfr[(kk + 1) & 1][i] = lds8(&sm.k[kb3][16 * i + lr][32 * (kk + 1) + 8 * lg]);
+          for (int i = 0; i < 4; ++i) kfr[(kk + 1) & 1][i] = lds8(&sm.k[kb3][16 * i + lr][32 * (kk + 1) + 8 * sg]);
         }
         sched_fence();
 #pragma unroll
@@ -278,10 +290,10 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
       }
       Ub[0] = pair_k32(to_h4(U[0]), to_h4(U[1]));
       Ub[1] = pair_k32(to_h4(U[2]), to_h4(U[3]));
-      *reinterpret_cast<h8*>(&sm.u[dv][8 * lg]) = Ub[0];
-      *reinterpret_cast<h8*>(&sm.u[dv][32 + 8 * lg]) = Ub[1];
+      *reinterpret_cast<h8*>(&sm.u[dv][8 * sg]) = Ub[0];
+      *reinterpret_cast<h8*>(&sm.u[dv][32 + 8 * sg]) = Ub[1];
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) kt0[kb] = lds8(&sm.kt[16 * kb + lr][8 * lg]);
+      for (int kb = 0; kb < 8; ++kb) kt0[kb] = lds8(&sm.kt[16 * kb + lr][8 * sg]);
       const float gC = g.gam[C - 1];
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) St[kb] *= gC;
@@ -292,7 +304,7 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
       const int n = (int)(T - t0 < C ? T - t0 : C);
       h8 kt1[8];
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) kt1[kb] = lds8(&sm.kt[16 * kb + lr][32 + 8 * lg]);
+      for (int kb = 0; kb < 8; ++kb) kt1[kb] = lds8(&sm.kt[16 * kb + lr][32 + 8 * sg]);
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) St[kb] = mfma32(kt1[kb], Ub[1], mfma32(kt0[kb], Ub[0], St[kb]));
       if (p.s_ckpt && n == C && ((t0 + n) % p.ckpt_every) == 0) {
@@ -304,7 +316,7 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         Sb[kk] = pair_k32(to_h4(St[2 * kk]), to_h4(St[2 * kk + 1]));
-        *reinterpret_cast<h8*>(&sm.s[dv][32 * kk + 8 * lg]) = Sb[kk];
+        *reinterpret_cast<h8*>(&sm.s[dv][32 * kk + 8 * sg]) = Sb[kk];
       }
     }
     __syncthreads();
@@ -327,7 +339,7 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t
 // LDS counter the barriers wait on).
 
 // Half of the row-major tokens of a chunk (rows 32 half + 0..31) of a [token][d_k] bf16 input,
-// converted to fp16 into an LDS tile.
+// converted to fp16 into a chunk-swizzled LDS tile (row 32 half + 4 i + rq has bit 2 = i & 1).
 template <int half>
 struct RowStage {
   __amdgpu_buffer_rsrc_t r;
@@ -341,14 +353,14 @@ struct RowStage {
   }
   __device__ __forceinline__ void store(_Float16 (*dst)[LQ]) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<h8*>(&dst[32 * half + 4 * i + rq][8 * ch]) = bf8_to_h8(x[i]);
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<h8*>(&dst[32 * half + 4 * i + rq][8 * (ch ^ (i & 1))]) = bf8_to_h8(x[i]);
   }
 };
 
 // Decayed, transposed keys for 4 d_k blocks kb0.. and one 32-token half kc of a chunk: transpose
 // reads from the row-major keys, each token scaled by e^{G_63 - G}.
 __device__ __forceinline__ void stage_kt(Smem& sm, const _Float16* k, const Gates& g, int kb0, int kc, int l) {
-  const int lr = l & 15, lg = l >> 4;
+  const int lr = l & 15, lg = l >> 4, sg = swl(l);
   const h4 a = to_h4(*reinterpret_cast<const f4*>(&g.dec[32 * kc + 8 * lg]));
   const h4 b = to_h4(*reinterpret_cast<const f4*>(&g.dec[32 * kc + 8 * lg + 4]));
   const h8 dech = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -356,7 +368,7 @@ __device__ __forceinline__ void stage_kt(Smem& sm, const _Float16* k, const Gate
   for (int j = 0; j < 4; ++j) {
     const int dk0 = 16 * (kb0 + j);
     const h8 x = __builtin_bit_cast(h8, frag8_tr(k, LQ, 32 * kc, dk0, l)) * dech;
-    *reinterpret_cast<h8*>(&sm.kt[dk0 + lr][32 * kc + 8 * lg]) = x;
+    *reinterpret_cast<h8*>(&sm.kt[dk0 + lr][32 * kc + 8 * sg]) = x;
   }
 }
 
@@ -367,7 +379,7 @@ __device__ __forceinline__ void stage_kt(Smem& sm, const _Float16* k, const Gate
 // c + 1 in phase 2 (each half is read by the chain in the phase after it is written).
 template <typename TOut, int tb0>
 __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, int64_t bh, int c0, int l, int64_t nchunks) {
-  const int lr = l & 15, lg = l >> 4;
+  const int lr = l & 15, lg = l >> 4, sg = swl(l);
   const int64_t T = p.T, tok0 = bh * T;
   const auto orr = __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<TOut*>(p.o) + tok0 * D), 0,
                                                      (int)(T * D * (int64_t)sizeof(TOut)), kRsrcWord3);
@@ -381,9 +393,9 @@ __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, int64_t b
       h8 fr[2][4];  // [step parity][q0 q1 s0 s1]
       auto ld = [&](int kk, h8 (&f)[4]) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) f[t] = lds8(&sm.q[16 * (tb0 + t) + lr][32 * kk + 8 * lg]);
+        for (int t = 0; t < 2; ++t) f[t] = lds8(&sm.q[16 * (tb0 + t) + lr][32 * kk + 8 * sg]);
 #pragma unroll
-        for (int d = 0; d < 2; ++d) f[2 + d] = lds8(&sm.s[16 * d + lr][32 * kk + 8 * lg]);
+        for (int d = 0; d < 2; ++d) f[2 + d] = lds8(&sm.s[16 * d + lr][32 * kk + 8 * sg]);
       };
       ld(0, fr[0]);
 #pragma unroll
@@ -412,9 +424,9 @@ __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, int64_t b
       const int tb = tb0 + t;
 #pragma unroll
       for (int kc = 0; kc <= (tb >> 1); ++kc) {  // P is zero above the diagonal blocks
-        const h8 pf = lds8(&sm.p[16 * tb + lr][32 * kc + 8 * lg]);
+        const h8 pf = lds8(&sm.p[16 * tb + lr][32 * kc + 8 * sg]);
 #pragma unroll
-        for (int d = 0; d < 2; ++d) Oa[t][d] = mfma32(lds8(&sm.u[16 * d + lr][32 * kc + 8 * lg]), pf, Oa[t][d]);
+        for (int d = 0; d < 2; ++d) Oa[t][d] = mfma32(lds8(&sm.u[16 * d + lr][32 * kc + 8 * sg]), pf, Oa[t][d]);
       }
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
@@ -469,7 +481,7 @@ __device__ __forceinline__ void tdiag_role(Smem& sm, int l, int64_t nchunks) {
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const h8 kf = lds8(&sm.k[kbuf(c + 2)][16 * (J0 + j) + lr][32 * kk + 8 * lg]);
+          const h8 kf = lds8(&sm.k[kbuf(c + 2)][16 * (J0 + j) + lr][32 * kk + 8 * swl(l)]);
           acc[j] = mfma32(kf, kf, acc[j]);
         }
 #pragma unroll
@@ -552,7 +564,9 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int6
   const auto br = stream_rsrc(p.beta, tok0, p.T);
   const auto gr = stream_rsrc(p.log_alpha, tok0, p.T);
   const auto vr = stream_rsrc(p.v, tok0 * D, p.T * D);
-  const int dq = l & 3, vq = l >> 2;    // values: channels c0 + 8 dq .., tokens 4 vq .. 4 vq + 3
+  // values: channels c0 + 8 dq .., tokens 4 vq .. 4 vq + 3; with the 16 token groups on
+  // consecutive lanes the transposed 8-byte stores are free of LDS bank conflicts
+  const int dq = l >> 4, vq = l & 15;
   struct Set {
     uint32_t bb, gg;
     v4u vv[4];
@@ -652,22 +666,23 @@ __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
   for (int c = -2; c < (int)nchunks; ++c) {
     {
       const Gates& g = sm.gt[kbuf(c)];
-      f4 fac[5], acc[5];  // decay factors first: their reads and exponentials overlap the MFMAs
-#pragma unroll
-      for (int t = 0; t < 2; ++t) fac[t] = diag_decay(g, PR[SET][t], lr, lg);
-#pragma unroll
-      for (int t = 2; t < 5; ++t) fac[t] = offdiag_p(g, PR[SET][t], PJ[SET][t], lr, lg, f4{1.f, 1.f, 1.f, 1.f});
+      f4 fac[5], acc[5];
 #pragma unroll
       for (int t = 0; t < 5; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
       {
         h8 kf[2][4], qf[2][4];
         auto ld = [&](int kk, h8 (&k4)[4], h8 (&q4)[4]) {
 #pragma unroll
-          for (int J = J0; J <= J1; ++J) k4[J] = lds8(&sm.k[kbuf(c)][16 * J + lr][32 * kk + 8 * lg]);
+          for (int J = J0; J <= J1; ++J) k4[J] = lds8(&sm.k[kbuf(c)][16 * J + lr][32 * kk + 8 * swl(l)]);
 #pragma unroll
-          for (int R = R0; R < 4; ++R) q4[R] = lds8(&sm.q[16 * R + lr][32 * kk + 8 * lg]);
+          for (int R = R0; R < 4; ++R) q4[R] = lds8(&sm.q[16 * R + lr][32 * kk + 8 * swl(l)]);
         };
         ld(0, kf[0], qf[0]);
+        sched_fence();
+#pragma unroll
+        for (int t = 0; t < 2; ++t) fac[t] = diag_decay(g, PR[SET][t], lr, lg);
+#pragma unroll
+        for (int t = 2; t < 5; ++t) fac[t] = offdiag_p(g, PR[SET][t], PJ[SET][t], lr, lg, f4{1.f, 1.f, 1.f, 1.f});
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           if (kk < 3) ld(kk + 1, kf[(kk + 1) & 1], qf[(kk + 1) & 1]);
@@ -679,7 +694,7 @@ __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
       }
 #pragma unroll
       for (int t = 0; t < 5; ++t)
-        *reinterpret_cast<h4*>(&sm.p[16 * PR[SET][t] + lr][16 * PJ[SET][t] + 4 * lg]) = to_h4(fac[t] * acc[t]);
+        *reinterpret_cast<h4*>(&sm.p[16 * PR[SET][t] + lr][16 * PJ[SET][t] + 4 * swl4(l)]) = to_h4(fac[t] * acc[t]);
     }
     __syncthreads();
     {
@@ -695,7 +710,7 @@ __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
         h8 kf[2][4];
         auto ld = [&](int kk, h8 (&k4)[4]) {
 #pragma unroll
-          for (int J = SET; J < 4; ++J) k4[J] = lds8(&sm.k[kb2][16 * J + lr][32 * kk + 8 * lg]);
+          for (int J = SET; J < 4; ++J) k4[J] = lds8(&sm.k[kb2][16 * J + lr][32 * kk + 8 * swl(l)]);
         };
         ld(0, kf[0]);
 #pragma unroll
@@ -733,7 +748,7 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
 
   // T and P start at zero; their upper blocks are never written
   for (int e = tid; e < 2 * C * LC / 8; e += NTH) reinterpret_cast<v4u*>(&sm.t[0][0][0])[e] = v4u{0u, 0u, 0u, 0u};
-  for (int e = tid; e < C * LC / 8; e += NTH) reinterpret_cast<v4u*>(&sm.p[0][0])[e] = v4u{0u, 0u, 0u, 0u};
+  for (int e = tid; e < C * LK / 8; e += NTH) reinterpret_cast<v4u*>(&sm.p[0][0])[e] = v4u{0u, 0u, 0u, 0u};
 
   // Every role runs nchunks + 2 iterations of two barriers after one initial barrier.  Waves w,
   // w + 4 and w + 8 share a SIMD: each chain (0, 1) shares its SIMD with an output wave (4, 5)
