@@ -15,6 +15,9 @@ Function status (see ``tests/test_oracle_pins.py`` for the pins):
   forward (KDA)  -- pinned: rational brute force of the printed KDA form, equal
                     channel gates == GDN, column-wise forget-only, exact overwrite.
   decode_step    -- pinned: exact overwrite; T single steps == one forward pass.
+  serving.*      -- the serving-side decode (slot-addressed states, grouped heads, fused
+                    gate activations and q/k normalisation, verify / commit windows): a
+                    composition of decode_step; pinned in tests/test_oracle_serving.py.
 """
 from __future__ import annotations
 
