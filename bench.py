@@ -108,7 +108,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "kda", "copy", "all"], default="all",
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "kda", "serving", "copy", "all"], default="all",
                     help="run a subset (for profiling); the JSON line needs 'all' or 'prefill'")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -269,6 +269,60 @@ def main():
                          "kernel": "kda_chunk_mfma_kernel", "algorithmic_bytes": nb},
             "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         log(f"kda prefill: {ms:.3f} ms")
+
+    # ---------------- serving-side decode windows: verify 4 draft tokens, commit, KDA step ----------------
+    if args.only in ("serving", "all"):
+        cv = synth.SERVING["verify"]
+        log("serving: generating inputs")
+        inp = synth.make_serving(cv.N, cv.T, cv.H, cv.Hqk, cv.D, cv.P, cv.dtype, raw=True, s_std=cv.s_std,
+                                 seed=2001)
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        o = torch.empty(cv.N, cv.T, cv.H, cv.D, dtype=torch.bfloat16, device=dev)
+        kw = dict(slots=d["slots"], qk_l2norm=True, A_log=d["A_log"], dt_bias=d["dt_bias"])
+        state_b = cv.D * cv.D * 4                         # one (sequence, head) state
+        tok_in = (2 * cv.Hqk * cv.D + cv.H * cv.D + 2 * cv.H) * 2   # q, k, v, b, a of one token (bf16)
+        tok_out = cv.H * cv.D * 2                         # o of one token (bf16)
+        ms_v = time_launches(lambda i: g.gdn_decode_verify(d["pool"], d["q"], d["k"], d["v"], d["beta"],
+                                                           d["log_alpha"], o=o, **kw), 20, 3, torch)
+        nb_v = cv.N * cv.H * state_b + cv.N * cv.T * (tok_in + tok_out) + 2 * cv.H * 4 + cv.N * 4
+
+        def commit(i):  # the same accepted counts each time: the states keep advancing
+            g.gdn_decode_commit(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["n_commit"], **kw)
+
+        ms_c = time_launches(commit, 20, 3, torch)
+        nc = inp["n_commit"].numpy()
+        nb_c = int(cv.N * cv.H * state_b + (nc > 0).sum() * cv.H * state_b + nc.sum() * tok_in
+                   + 2 * cv.H * 4 + 2 * cv.N * 4)
+        del d, o, inp
+        torch.cuda.empty_cache()
+        ck = synth.SERVING["kda"]
+        inp = synth.make_serving(ck.N, ck.T, ck.H, ck.Hqk, ck.D, ck.P, ck.dtype, kda=True, s_std=ck.s_std,
+                                 seed=2002)
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        o = torch.empty(ck.N, ck.T, ck.H, ck.D, dtype=torch.bfloat16, device=dev)
+        ms_k = time_launches(lambda i: g.gdn_decode_ex(d["pool"], d["q"], d["k"], d["v"], d["beta"],
+                                                       d["log_alpha"], kda=True, o=o), 20, 3, torch)
+        nb_k = 2 * ck.N * ck.H * ck.D * ck.D * 4 + ck.N * (2 * ck.Hqk * ck.D + 2 * ck.H * ck.D + ck.H
+                                                           + ck.H * ck.D) * 2
+
+        def rec(name, cfg, ms, nb, **more):
+            gb = nb / (ms * 1e-3) / 1e9
+            r = {"workload": cfg.name, "N": cfg.N, "H": cfg.H, "H_qk": cfg.Hqk, "d": cfg.D, "T": cfg.T,
+                 "pool_rows": cfg.P, "us": round(ms * 1e3, 2),
+                 "roofline": {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(gb / HBM_PEAK_GBS, 4), "traffic": None,
+                              "kernel": "decode_ex_kernel", "algorithmic_bytes": int(nb)}}
+            r.update(more)
+            log(f"serving {name}: {ms * 1e3:.1f} us, {gb:.0f} GB/s, HBM frac {gb / HBM_PEAK_GBS:.3f}")
+            return r
+
+        extra["serving_decode"] = {
+            "verify": rec("verify", cv, ms_v, nb_v, draft_tokens=cv.T, fused="q/k L2 norm, gate activations"),
+            "commit": rec("commit", cv, ms_c, nb_c, accepted_tokens=int(nc.sum())),
+            "kda_step": rec("kda step", ck, ms_k, nb_k),
+        }
+        del d, o, inp
+        torch.cuda.empty_cache()
 
     # ---------------- plain device copy of known size: calibrates the HBM byte counters ----------------
     if args.only == "copy":

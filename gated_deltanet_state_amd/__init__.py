@@ -19,7 +19,8 @@ __all__ = [
     "GdnError", "gdn_chunk_fwd", "kda_chunk_fwd", "gdn_decode_step", "gdn_chunk_workspace_size",
     "gdn_status_string", "gdn_version", "library_path", "lib",
     "GDN_F32", "GDN_BF16", "GDN_SUCCESS", "GDN_ERROR_INVALID_VALUE", "GDN_ERROR_NOT_SUPPORTED",
-    "GDN_ERROR_HIP", "GdnChunkDesc",
+    "GDN_ERROR_HIP", "GdnChunkDesc", "GdnDecodeExDesc", "gdn_decode_ex", "gdn_decode_verify",
+    "gdn_decode_commit",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +37,17 @@ class GdnChunkDesc(ctypes.Structure):
         ("Dk", ctypes.c_int64), ("Dv", ctypes.c_int64),
         ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
         ("ckpt_every", ctypes.c_int64),
+    ]
+
+
+class GdnDecodeExDesc(ctypes.Structure):
+    """Mirror of gdn_decode_ex_desc_t."""
+    _fields_ = [
+        ("N", ctypes.c_int64), ("H", ctypes.c_int64), ("H_qk", ctypes.c_int64), ("Dk", ctypes.c_int64),
+        ("Dv", ctypes.c_int64), ("T", ctypes.c_int64), ("P", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+        ("kda", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32), ("raw_gates", ctypes.c_int32),
+        ("write_state", ctypes.c_int32),
     ]
 
 
@@ -61,6 +73,8 @@ def _load() -> ctypes.CDLL:
         f.restype = ci
     L.gdn_decode_step.argtypes = [i64, i64, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gdn_decode_step.restype = ci
+    L.gdn_decode_ex.argtypes = [ctypes.POINTER(GdnDecodeExDesc)] + [vp] * 12
+    L.gdn_decode_ex.restype = ci
     L.gdn_status_string.argtypes = [ci]
     L.gdn_status_string.restype = ctypes.c_char_p
     L.gdn_version.argtypes = []
@@ -211,3 +225,56 @@ def gdn_decode_step(state, q, k, v, beta, log_alpha, *, o=None, out_dtype=None, 
     if st != GDN_SUCCESS:
         raise GdnError(st, "gdn_decode_step")
     return o
+
+
+def gdn_decode_ex(pool, q, k, v, beta, log_alpha, *, slots=None, n_commit=None, write_state: bool = True,
+                  kda: bool = False, qk_l2norm: bool = False, A_log=None, dt_bias=None, o=None,
+                  out_dtype=None, return_o: bool = True, stream=None):
+    """Serving-side decode window (gdn_decode_ex in include/gdn.h).
+
+    pool [P,H,D,D] fp32 (rows slots[n] read, and written when write_state); q, k [N,T,Hqk,D];
+    v [N,T,H,D]; beta [N,T,H]; log_alpha [N,T,H] or [N,T,H,D] (kda); with A_log and dt_bias
+    ([H] fp32) given, beta and log_alpha are the raw b and a of the layer.  slots, n_commit:
+    int32 [N] or None.  Returns o [N,T,H,D] (or None when return_o is False and o is None).
+    """
+    if q.dim() != 4 or pool.dim() != 4:
+        raise ValueError("q must be [N, T, Hqk, D] and pool [P, H, D, D]")
+    N, T, Hqk, D = q.shape
+    P, H = pool.shape[0], pool.shape[1]
+    dev, in_dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    _check(pool, "pool", (P, H, D, D), torch.float32, dev)
+    for name, t, shp in (("k", k, (N, T, Hqk, D)), ("v", v, (N, T, H, D)), ("beta", beta, (N, T, H)),
+                         ("log_alpha", log_alpha, (N, T, H, D) if kda else (N, T, H))):
+        _check(t, name, shp, in_dt, dev)
+    raw = A_log is not None
+    if raw:
+        _check(A_log, "A_log", (H,), torch.float32, dev)
+        _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    for name, t in (("slots", slots), ("n_commit", n_commit)):
+        if t is not None:
+            _check(t, name, (N,), torch.int32, dev)
+    out_dt = out_dtype or in_dt
+    if o is None and return_o:
+        o = torch.empty(N, T, H, D, dtype=out_dt, device=dev)
+    if o is not None:
+        _check(o, "o", (N, T, H, D), out_dt, dev)
+    d = GdnDecodeExDesc(N, H, Hqk, D, D, T, P, _code(in_dt), _code(out_dt), int(kda), int(qk_l2norm),
+                        int(raw), int(write_state))
+    st = lib.gdn_decode_ex(ctypes.byref(d), _ptr(pool), _ptr(slots), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                           _ptr(log_alpha), _ptr(A_log), _ptr(dt_bias), _ptr(n_commit), _ptr(o), _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GdnError(st, "gdn_decode_ex")
+    return o
+
+
+def gdn_decode_verify(pool, q, k, v, beta, log_alpha, **kw):
+    """Outputs of all T draft tokens of each sequence; the pool is only read."""
+    return gdn_decode_ex(pool, q, k, v, beta, log_alpha, write_state=False, **kw)
+
+
+def gdn_decode_commit(pool, q, k, v, beta, log_alpha, n_commit, **kw):
+    """Apply the first n_commit[n] tokens of each window to the pool rows in place."""
+    kw.setdefault("return_o", False)
+    return gdn_decode_ex(pool, q, k, v, beta, log_alpha, n_commit=n_commit, write_state=True, **kw)

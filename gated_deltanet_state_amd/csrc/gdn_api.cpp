@@ -162,6 +162,51 @@ gdn_status_t gdn_decode_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv, gdn_d
   return e == hipSuccess ? GDN_SUCCESS : GDN_ERROR_HIP;
 }
 
+gdn_status_t gdn_decode_ex(const gdn_decode_ex_desc_t* d, float* pool, const int32_t* slots,
+                           const void* q, const void* k, const void* v, const void* beta,
+                           const void* log_alpha, const float* A_log, const float* dt_bias,
+                           const int32_t* n_commit, void* o, void* stream) {
+  if (!d) return GDN_ERROR_INVALID_VALUE;
+  if (d->N < 0 || d->H <= 0 || d->H_qk <= 0 || d->Dk <= 0 || d->Dv <= 0 || d->T <= 0 || d->P < 0)
+    return GDN_ERROR_INVALID_VALUE;
+  if (d->H % d->H_qk != 0) return GDN_ERROR_INVALID_VALUE;
+  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return GDN_ERROR_INVALID_VALUE;
+  for (int32_t f : {d->kda, d->qk_l2norm, d->raw_gates, d->write_state})
+    if (f != 0 && f != 1) return GDN_ERROR_INVALID_VALUE;
+  int64_t tok, rows, tmp;
+  if (!mul_ok(d->N, d->T, &tok) || !mul_ok(tok, d->H, &rows) || !mul_ok(rows, d->Dk, &tmp) ||
+      !mul_ok(d->P, d->H, &tmp) || !mul_ok(tmp, d->Dk * d->Dv, &tmp))
+    return GDN_ERROR_INVALID_VALUE;
+  if (d->Dk != d->Dv) return GDN_ERROR_NOT_SUPPORTED;
+  if (d->Dk != 16 && d->Dk != 32 && d->Dk != 64 && d->Dk != 128) return GDN_ERROR_NOT_SUPPORTED;
+  if (d->kda && d->raw_gates) return GDN_ERROR_NOT_SUPPORTED;
+  if (!slots && d->P < d->N) return GDN_ERROR_INVALID_VALUE;
+  if (d->N == 0 || d->P == 0 || (!d->write_state && !o)) return GDN_SUCCESS;
+  if (!pool || !q || !k || !v || !beta || !log_alpha) return GDN_ERROR_INVALID_VALUE;
+  if (d->raw_gates && (!A_log || !dt_bias)) return GDN_ERROR_INVALID_VALUE;
+  const gdn_dtype_t it = d->in_dtype;
+  if (!aligned16(pool) || !aligned_elem(q, it) || !aligned_elem(k, it) || !aligned_elem(v, it) ||
+      !aligned_elem(beta, it) || !aligned_elem(log_alpha, it) || (o && !aligned_elem(o, d->out_dtype)) ||
+      (slots && !aligned_elem(slots, GDN_F32)) || (n_commit && !aligned_elem(n_commit, GDN_F32)) ||
+      (d->raw_gates && (!aligned_elem(A_log, GDN_F32) || !aligned_elem(dt_bias, GDN_F32))))
+    return GDN_ERROR_INVALID_VALUE;
+  const size_t pool_bytes = (size_t)(d->P * d->H) * (size_t)(d->Dk * d->Dv) * sizeof(float);
+  const size_t o_bytes = (size_t)rows * (size_t)d->Dv * (d->out_dtype == GDN_F32 ? 4 : 2);
+  if (o && overlaps(pool, pool_bytes, o, o_bytes)) return GDN_ERROR_INVALID_VALUE;
+  gdn::DecodeExArgs a;
+  memset(&a, 0, sizeof a);
+  a.N = d->N; a.H = d->H; a.Hqk = d->H_qk; a.D = d->Dk; a.T = d->T; a.P = d->P;
+  a.in_dtype = d->in_dtype; a.out_dtype = d->out_dtype;
+  a.kda = d->kda; a.qk_l2norm = d->qk_l2norm; a.raw_gates = d->raw_gates; a.write_state = d->write_state;
+  a.pool = pool; a.slots = slots; a.n_commit = n_commit;
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
+  a.A_log = d->raw_gates ? A_log : nullptr;
+  a.dt_bias = d->raw_gates ? dt_bias : nullptr;
+  a.o = o;
+  hipError_t e = gdn::launch_decode_ex(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GDN_SUCCESS : GDN_ERROR_HIP;
+}
+
 const char* gdn_status_string(gdn_status_t s) {
   switch (s) {
     case GDN_SUCCESS: return "success";

@@ -159,6 +159,160 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ st
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Serving-side decode: a window of T tokens per sequence on states addressed through a slot
+// table, with value heads sharing query/key heads, optionally with the q/k normalisation and
+// the gate activations of the layer fused in, and either applying the first n_commit tokens
+// to the state (commit) or leaving it untouched (verification of draft tokens).
+//   * A sequence whose slot is negative or past the pool is skipped (no output written).
+//   * Value head h reads query/key head h / (H / Hqk).
+//   * Normalisation: x / sqrt(sum x^2 + 1e-6) over the head dimension ("Attention, Part 4",
+//     a Gated DeltaNet layer normalises queries and keys to length 1).
+//   * Gate activations ("Attention, Part 4", section "Where alpha and beta come from"):
+//     beta = sigmoid(b), log alpha = -exp(A_log[h]) softplus(a + dt_bias[h]).
+//   * KDA scales key channel j of the state by alpha_j before the step ("From Traditional
+//     Attention to hybrid ones", section 7); the step is then the scalar one with alpha = 1.
+// The state is read once and, on commit, written once: the tokens of the window run on the
+// registers, each with the reductions of the single-step kernel above.  The state after the
+// last committed token is stored as soon as it exists.
+template <int D, typename TIn, typename TOut, bool KDA>
+__global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
+  constexpr int LPR = D / 4, RG = 8, TPS = LPR * RG, SPB = kThreads / TPS, RPT = D / RG;
+  static_assert(2 * RPT == LPR, "one reduced value per lane");
+  __shared__ float ush[SPB][D];
+
+  const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
+  const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
+  const TIn* __restrict__ v = static_cast<const TIn*>(a.v);
+  const TIn* __restrict__ beta = static_cast<const TIn*>(a.beta);
+  const TIn* __restrict__ log_alpha = static_cast<const TIn*>(a.log_alpha);
+  TOut* __restrict__ o = static_cast<TOut*>(a.o);
+
+  const int tid = threadIdx.x;
+  const int lane_slot = tid / TPS;
+  const int64_t s = static_cast<int64_t>(blockIdx.x) * SPB + lane_slot;  // (sequence, value head)
+  if (s >= a.N * a.H) return;  // whole lane groups drop out together
+  const int64_t n = s / a.H, h = s - n * a.H, hq = h / (a.H / a.Hqk);
+  const int64_t row_slot = a.slots ? static_cast<int64_t>(a.slots[n]) : n;
+  if (row_slot < 0 || row_slot >= a.P) return;
+  int ncommit = 0;
+  if (a.write_state) {
+    ncommit = a.n_commit ? a.n_commit[n] : static_cast<int>(a.T);
+    ncommit = ncommit < 0 ? 0 : (ncommit > a.T ? static_cast<int>(a.T) : ncommit);
+  }
+  const int tend = o ? static_cast<int>(a.T) : ncommit;
+  if (tend == 0) return;
+
+  const int lt = tid % TPS, c4 = lt % LPR, rg = lt / LPR;
+  f4v* S = reinterpret_cast<f4v*>(a.pool + (row_slot * a.H + h) * D * D);
+  f4v st[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(&S[(rg + RG * i) * LPR + c4]);
+  float A = 0.f, dtb = 0.f;
+  if (!KDA && a.raw_gates) {
+    A = __expf(a.A_log[h]);
+    dtb = a.dt_bias[h];
+  }
+
+  for (int t = 0; t < tend; ++t) {
+    const int64_t tok = n * a.T + t;
+    const int64_t qk0 = (tok * a.Hqk + hq) * D, g0 = tok * a.H + h;
+    float kk[4], qq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kk[j] = ld_in(k, qk0 + 4 * c4 + j);
+      qq[j] = ld_in(q, qk0 + 4 * c4 + j);
+    }
+    if (a.qk_l2norm) {
+      const float nk = group_sum<LPR>(kk[0] * kk[0] + kk[1] * kk[1] + kk[2] * kk[2] + kk[3] * kk[3]);
+      const float nq = group_sum<LPR>(qq[0] * qq[0] + qq[1] * qq[1] + qq[2] * qq[2] + qq[3] * qq[3]);
+      const float rk = 1.f / sqrtf(nk + 1e-6f), rq = 1.f / sqrtf(nq + 1e-6f);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kk[j] *= rk;
+        qq[j] *= rq;
+      }
+    }
+    float b = ld_in(beta, g0), dec = 1.f;
+    if constexpr (KDA) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float al = expf(ld_in(log_alpha, g0 * D + 4 * c4 + j));
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) st[i][j] *= al;
+      }
+    } else {
+      float g = ld_in(log_alpha, g0);
+      if (a.raw_gates) {
+        b = 1.f / (1.f + expf(-b));
+        const float x = g + dtb;
+        g = -A * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))));  // softplus, no overflow
+      }
+      dec = expf(g);
+    }
+
+    float vals[2 * RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      vals[2 * i] = st[i][0] * kk[0] + st[i][1] * kk[1] + st[i][2] * kk[2] + st[i][3] * kk[3];
+      vals[2 * i + 1] = st[i][0] * qq[0] + st[i][1] * qq[1] + st[i][2] * qq[2] + st[i][3] * qq[3];
+    }
+    const float kq = group_sum<LPR>(kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3]);
+    reduce_scatter<LPR>(vals, c4);
+    const int row = rg + RG * (c4 >> 1);
+    const float r_or_p = vals[0];
+    const float u = b * (ld_in(v, (tok * a.H + h) * D + row) - dec * r_or_p);
+    const float u_even = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(u), 0xA0, 0xf, 0xf, false));
+    if (c4 & 1) {
+      if (o) st_out(o, (tok * a.H + h) * D + row, dec * r_or_p + u_even * kq);
+    } else {
+      ush[lane_slot][row] = u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const float ui = ush[lane_slot][rg + RG * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st[i][j] = dec * st[i][j] + ui * kk[j];
+    }
+    // the next token overwrites the corrections only after every lane has read them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (t + 1 == ncommit) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) __builtin_nontemporal_store(st[i], &S[(rg + RG * i) * LPR + c4]);
+    }
+  }
+}
+
+template <int D, typename TIn, typename TOut>
+hipError_t launch_decode_ex_t(const DecodeExArgs& a, hipStream_t stream) {
+  constexpr int SPB = kThreads / (2 * D);
+  const int64_t units = a.N * a.H;
+  const int64_t blocks = (units + SPB - 1) / SPB;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (a.kda)
+    hipLaunchKernelGGL((decode_ex_kernel<D, TIn, TOut, true>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((decode_ex_kernel<D, TIn, TOut, false>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_ex_d(const DecodeExArgs& a, hipStream_t s) {
+  if (a.in_dtype == GDN_BF16) {
+    return a.out_dtype == GDN_BF16 ? launch_decode_ex_t<D, __hip_bfloat16, __hip_bfloat16>(a, s)
+                                   : launch_decode_ex_t<D, __hip_bfloat16, float>(a, s);
+  }
+  return a.out_dtype == GDN_BF16 ? launch_decode_ex_t<D, float, __hip_bfloat16>(a, s)
+                                 : launch_decode_ex_t<D, float, float>(a, s);
+}
+
 template <int D, typename TIn, typename TOut>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int SPB = kThreads / (2 * D);
@@ -187,6 +341,16 @@ hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
 
 bool decode_supported(const DecodeArgs& a) {
   return a.D == 16 || a.D == 32 || a.D == 64 || a.D == 128;
+}
+
+hipError_t launch_decode_ex(const DecodeExArgs& a, hipStream_t s) {
+  switch (a.D) {
+    case 16: return launch_decode_ex_d<16>(a, s);
+    case 32: return launch_decode_ex_d<32>(a, s);
+    case 64: return launch_decode_ex_d<64>(a, s);
+    case 128: return launch_decode_ex_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {

@@ -31,6 +31,19 @@ struct DecodeArgs {
   void* o;
 };
 
+// Serving-side decode window (see gdn_decode_ex in gdn.h), after host-side validation.
+struct DecodeExArgs {
+  int64_t N, H, Hqk, D, T, P;  // P: rows of the state pool
+  gdn_dtype_t in_dtype, out_dtype;
+  int kda, qk_l2norm, raw_gates, write_state;
+  float* pool;
+  const int32_t* slots;     // may be null (slot n = n)
+  const int32_t* n_commit;  // may be null (all T tokens)
+  const void *q, *k, *v, *beta, *log_alpha;
+  const float *A_log, *dt_bias;  // raw gates only
+  void* o;                  // may be null
+};
+
 // Matrix-core prefill (bf16 inputs, D = 128, chunk = 64).
 bool chunk_mfma_supported(const ChunkArgs& a);
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool kda, hipStream_t stream);
@@ -43,5 +56,6 @@ hipError_t launch_chunk_valu(const ChunkArgs& a, bool kda, hipStream_t stream);
 // Decode step (D in {16,32,64,128}).
 bool decode_supported(const DecodeArgs& a);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_ex(const DecodeExArgs& a, hipStream_t stream);
 
 }  // namespace gdn

@@ -119,3 +119,64 @@ def make_workload(index: int):
                            seed=seed_of(index))
     return make_prefill(c.B, c.H, c.T, c.Dk, c.Dv, c.dtype, kda=c.kda, s0_std=c.s0_std,
                         seed=seed_of(index))
+
+
+@dataclass(frozen=True)
+class ServingConfig:
+    """A window of T tokens for N live sequences whose fp32 states sit in a pool of P rows."""
+    name: str
+    N: int
+    H: int
+    Hqk: int
+    D: int
+    T: int
+    P: int
+    dtype: torch.dtype
+    s_std: float
+    kda: bool = False
+    raw: bool = False
+
+
+# Serving-side decode workloads (the decode workload's 256 sequences x 32 value heads x
+# 128x128 states): speculative verification of 4 draft tokens with 16 query/key heads and
+# the raw gate projections; a KDA decode step.
+SERVING = {
+    "verify": ServingConfig("gdn_decode_verify4_bf16", 256, 32, 16, 128, 4, 512, torch.bfloat16, 0.02, raw=True),
+    "kda": ServingConfig("kda_decode_bf16", 256, 32, 32, 128, 1, 256, torch.bfloat16, 0.02, kda=True),
+}
+
+
+def make_serving(N: int, T: int, H: int, Hqk: int, D: int, P: int, dtype: torch.dtype = torch.bfloat16, *,
+                 kda: bool = False, raw: bool = False, s_std: float = 0.02, seed: int = 0,
+                 skip_every: int = 0) -> Dict[str, Optional[torch.Tensor]]:
+    """Draw, in order: the state pool, a slot table (N distinct rows of the pool, every
+    skip_every-th sequence marked -1), accepted-token counts in 0..T, then q, k, v and the
+    gates of every token.  With ``raw`` the gates are the layer's raw projections b, a
+    (N(0, 1)) with per-head A_log ~ U[-1, 1] and dt_bias ~ U[-4, -2], and q, k are left
+    unnormalised (3 N(0, 1)); otherwise beta = sigmoid(N(0, 1)), log alpha ~ U[-0.2, -0.005]
+    (per key channel for KDA) and q, k have unit length."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    pool = torch.randn(P, H, D, D, generator=g) * s_std
+    slots = torch.randperm(P, generator=g)[:N].to(torch.int32)
+    if skip_every > 0:
+        slots[::skip_every] = -1
+    n_commit = torch.randint(0, T + 1, (N,), generator=g).to(torch.int32)
+    if raw:
+        q = torch.randn(N, T, Hqk, D, generator=g) * 3
+        k = torch.randn(N, T, Hqk, D, generator=g) * 3
+    else:
+        q = _unit(torch.randn(N, T, Hqk, D, generator=g))
+        k = _unit(torch.randn(N, T, Hqk, D, generator=g))
+    v = torch.randn(N, T, H, D, generator=g)
+    A_log = dt_bias = None
+    if raw:
+        beta = torch.randn(N, T, H, generator=g)
+        log_alpha = torch.randn(N, T, H, generator=g)
+        A_log = torch.rand(H, generator=g) * 2 - 1
+        dt_bias = torch.rand(H, generator=g) * 2 - 4
+    else:
+        beta = torch.sigmoid(torch.randn(N, T, H, generator=g))
+        log_alpha = torch.rand(*((N, T, H, D) if kda else (N, T, H)), generator=g) * 0.195 - 0.2
+    return {"pool": pool, "slots": slots, "n_commit": n_commit, "q": q.to(dtype), "k": k.to(dtype),
+            "v": v.to(dtype), "beta": beta.to(dtype), "log_alpha": log_alpha.to(dtype),
+            "A_log": A_log, "dt_bias": dt_bias}

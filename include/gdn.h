@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 100 /* 1.0.0 */
+#define GDN_VERSION 110 /* 1.1.0 */
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
 
@@ -142,6 +142,57 @@ gdn_status_t gdn_decode_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv, gdn_d
                              gdn_dtype_t out_dtype, float* state, const void* q, const void* k,
                              const void* v, const void* beta, const void* log_alpha, void* o,
                              void* stream);
+
+/*
+ * Serving-side decode: a window of T tokens for each of N live sequences whose states sit
+ * in a pool addressed through a slot table.  It covers
+ *  - one decode step per sequence on slot-addressed states (T = 1): the state is fixed per
+ *    live sequence and updated in place ("From Traditional Attention to hybrid ones",
+ *    section "vLLM Storage");
+ *  - verification of T draft tokens without touching the state (write_state = 0), then a
+ *    commit of the n_commit[n] accepted ones (write_state = 1): speculative decoding needs
+ *    the state from before the draft ("Hybrid models: what Gated DeltaNet replaces in the
+ *    KV cache", section "What a recurrent state changes for serving"), and a verified but
+ *    rejected token is simply never committed;
+ *  - value heads sharing query/key heads (H a multiple of H_qk, value head h reads q/k head
+ *    h / (H / H_qk));
+ *  - KDA's per-channel decay (kda = 1; "From Traditional Attention to hybrid ones",
+ *    section 7);
+ *  - the layer's q/k normalisation and gate activations fused in ("Attention, Part 4",
+ *    section "Where alpha and beta come from": beta = sigmoid(b), log alpha =
+ *    -exp(A_log) softplus(a + dt_bias); queries and keys normalised to length 1, here as
+ *    x / sqrt(sum x^2 + 1e-6)).
+ *
+ *   pool      [P, H, Dv, Dk] fp32; row slots[n] is read, and written when write_state = 1
+ *   slots     [N] int32 pool row of sequence n, or NULL for row n (then P >= N).  A
+ *             negative row or one >= P skips the sequence: nothing is read or written
+ *   q, k      [N, T, H_qk, Dk]   in_dtype (raw when qk_l2norm = 1)
+ *   v         [N, T, H, Dv]      in_dtype
+ *   beta      [N, T, H]          in_dtype (b when raw_gates = 1)
+ *   log_alpha [N, T, H], or [N, T, H, Dk] when kda = 1, in_dtype (a when raw_gates = 1)
+ *   A_log, dt_bias [H] fp32, required when raw_gates = 1, ignored otherwise
+ *   n_commit  [N] int32 tokens to commit (clamped to 0..T), or NULL for all T; used only
+ *             when write_state = 1.  The row becomes the state after those tokens; with 0
+ *             it is left as it was.
+ *   o         [N, T, H, Dv] out_dtype, output of every token of the window, or NULL (then
+ *             the kernel stops after the committed tokens).  Rows of skipped sequences are
+ *             not written.
+ * Token t of a sequence sees the state after its tokens 0..t-1 of this window.  Supported:
+ * Dk == Dv in {16, 32, 64, 128}; raw_gates with kda is NOT_SUPPORTED.  Two sequences
+ * must not share a slot in one call (their writes would race).  N = 0, or o = NULL with
+ * write_state = 0, is a no-op.
+ */
+typedef struct {
+  int64_t N, H, H_qk, Dk, Dv, T, P;
+  gdn_dtype_t in_dtype;  /* dtype of q, k, v, beta, log_alpha */
+  gdn_dtype_t out_dtype; /* dtype of o */
+  int32_t kda, qk_l2norm, raw_gates, write_state; /* each 0 or 1 */
+} gdn_decode_ex_desc_t;
+
+gdn_status_t gdn_decode_ex(const gdn_decode_ex_desc_t* d, float* pool, const int32_t* slots,
+                           const void* q, const void* k, const void* v, const void* beta,
+                           const void* log_alpha, const float* A_log, const float* dt_bias,
+                           const int32_t* n_commit, void* o, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* gdn_status_string(gdn_status_t s);

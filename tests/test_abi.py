@@ -24,8 +24,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
-        "gdn_chunk_fwd", "gdn_chunk_workspace_size", "gdn_decode_step", "gdn_status_string",
-        "gdn_version", "kda_chunk_fwd"])
+        "gdn_chunk_fwd", "gdn_chunk_workspace_size", "gdn_decode_ex", "gdn_decode_step",
+        "gdn_status_string", "gdn_version", "kda_chunk_fwd"])
 
 
 def test_library_exports_every_declared_symbol(g):
@@ -37,10 +37,12 @@ def test_library_exports_every_declared_symbol(g):
 def test_desc_struct_layout(g):
     assert ctypes.sizeof(g.GdnChunkDesc) == 64
     assert g.GdnChunkDesc.ckpt_every.offset == 56
+    assert ctypes.sizeof(g.GdnDecodeExDesc) == 80
+    assert g.GdnDecodeExDesc.in_dtype.offset == 56 and g.GdnDecodeExDesc.write_state.offset == 76
 
 
 def test_version_and_status_strings(g):
-    assert g.gdn_version() == 100
+    assert g.gdn_version() == 110
     for s in range(4):
         assert isinstance(g.gdn_status_string(s), str) and g.gdn_status_string(s)
     assert g.gdn_status_string(99) == "unknown status"
@@ -121,3 +123,42 @@ def test_decode_validation_errors(g):
     q[6] = ctypes.c_void_p(FAKE + 64)         # o inside the state
     assert f(2, 2, 128, 128, 1, 1, *q, None) == INV
     assert f(0, 2, 128, 128, 1, 1, *p, None) == g.GDN_SUCCESS  # no-op
+
+
+def _ex_desc(g, **kw):
+    base = dict(N=4, H=4, H_qk=2, Dk=128, Dv=128, T=2, P=8, in_dtype=g.GDN_BF16, out_dtype=g.GDN_BF16,
+                kda=0, qk_l2norm=0, raw_gates=0, write_state=1)
+    base.update(kw)
+    return g.GdnDecodeExDesc(**base)
+
+
+def _ex_call(g, d, **ptrs):
+    names = ["pool", "slots", "q", "k", "v", "beta", "log_alpha", "A_log", "dt_bias", "n_commit", "o"]
+    p = {n: FAKE + i * 0x1000000 for i, n in enumerate(names)}
+    p.update(ptrs)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return g.lib.gdn_decode_ex(None if d is None else ctypes.byref(d), *[v(p[n]) for n in names], None)
+
+
+def test_decode_ex_validation_errors(g):
+    INV, NS, OK = g.GDN_ERROR_INVALID_VALUE, g.GDN_ERROR_NOT_SUPPORTED, g.GDN_SUCCESS
+    assert _ex_call(g, None) == INV
+    assert _ex_call(g, _ex_desc(g, H=3, H_qk=2)) == INV            # H not a multiple of H_qk
+    assert _ex_call(g, _ex_desc(g, H_qk=0)) == INV
+    assert _ex_call(g, _ex_desc(g, T=0)) == INV
+    assert _ex_call(g, _ex_desc(g, P=-1)) == INV
+    assert _ex_call(g, _ex_desc(g, kda=2)) == INV
+    assert _ex_call(g, _ex_desc(g, in_dtype=9)) == INV
+    assert _ex_call(g, _ex_desc(g, Dk=128, Dv=64)) == NS
+    assert _ex_call(g, _ex_desc(g, Dk=96, Dv=96)) == NS
+    assert _ex_call(g, _ex_desc(g, kda=1, raw_gates=1)) == NS
+    assert _ex_call(g, _ex_desc(g, P=2), slots=None) == INV          # identity slots need P >= N
+    assert _ex_call(g, _ex_desc(g), q=None) == INV
+    assert _ex_call(g, _ex_desc(g), pool=FAKE + 8) == INV             # misaligned pool
+    assert _ex_call(g, _ex_desc(g), slots=FAKE + 0x1000002) == INV   # misaligned int32 table
+    assert _ex_call(g, _ex_desc(g, raw_gates=1), A_log=None) == INV
+    assert _ex_call(g, _ex_desc(g), o=FAKE + 64) == INV               # o inside the pool
+    # no-ops: empty batch, empty pool, verification without outputs
+    assert _ex_call(g, _ex_desc(g, N=0)) == OK
+    assert _ex_call(g, _ex_desc(g, P=0)) == OK
+    assert _ex_call(g, _ex_desc(g, write_state=0), o=None) == OK

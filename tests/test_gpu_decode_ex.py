@@ -1,0 +1,140 @@
+"""Serving-side decode windows on the GPU (gdn_decode_ex through the C ABI) vs the fp64 oracle:
+slot-addressed states, grouped heads, KDA, fused gate activations and q/k normalisation,
+verification of draft tokens and commit of the accepted ones."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import serving
+from gated_deltanet_state_amd import synth
+from helpers import rel_l2, say, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    oracle.build(force=False)
+
+
+def _cuda(d):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def _ref(inp, *, kda, raw, write_state, n_commit=True, l2=None):
+    pool = inp["pool"].double().numpy().copy()
+    o = serving.decode_window(pool, inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"],
+                              slots=inp["slots"], kda=kda, n_commit=inp["n_commit"] if n_commit else None,
+                              write_state=write_state, qk_l2norm=raw if l2 is None else l2, raw_gates=raw,
+                              A_log=inp["A_log"], dt_bias=inp["dt_bias"])
+    return o, pool
+
+
+def _live(inp):
+    s = inp["slots"].numpy()
+    return np.nonzero((s >= 0) & (s < inp["pool"].shape[0]))[0]
+
+
+@pytest.mark.parametrize("D", [16, 64, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("kda,raw", [(False, False), (True, False), (False, True)])
+def test_window_verify_then_commit(D, dtype, kda, raw):
+    import gated_deltanet_state_amd as g
+    N, T, H, Hqk, P = 7, 3, 4, 2, 12
+    say(f"decode_ex D={D} dtype={dtype} kda={kda} raw={raw}")
+    inp = synth.make_serving(N, T, H, Hqk, D, P, dtype, kda=kda, raw=raw, seed=D + 7 * kda + 13 * raw,
+                             skip_every=3)
+    d = _cuda(inp)
+    kw = dict(slots=d["slots"], kda=kda, qk_l2norm=raw, A_log=d["A_log"], dt_bias=d["dt_bias"],
+              out_dtype=torch.float32)
+    live = _live(inp)
+    # verification: outputs of every draft token, the pool untouched bit for bit
+    pool0 = d["pool"].clone()
+    o = torch.full((N, T, H, D), 7.0, device="cuda")
+    g.gdn_decode_verify(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], o=o, **kw)
+    torch.cuda.synchronize()
+    o_ref, _ = _ref(inp, kda=kda, raw=raw, write_state=False)
+    assert torch.equal(d["pool"], pool0)
+    skipped = np.setdiff1d(np.arange(N), live)
+    assert bool((o[torch.as_tensor(skipped)] == 7.0).all())
+    tol = 1e-5 if dtype == torch.float32 else 2e-3
+    assert rel_l2(o[torch.as_tensor(live)], o_ref[live]) <= tol
+    # commit of the accepted tokens: pool rows of live sequences advance, the others stay
+    g.gdn_decode_commit(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["n_commit"], **kw)
+    torch.cuda.synchronize()
+    _, pool_ref = _ref(inp, kda=kda, raw=raw, write_state=True)
+    used = inp["slots"].numpy()[live]
+    untouched = np.setdiff1d(np.arange(P), used)
+    assert torch.equal(d["pool"][torch.as_tensor(untouched)], pool0[torch.as_tensor(untouched)])
+    zero = used[inp["n_commit"].numpy()[live] == 0]
+    if len(zero):
+        assert torch.equal(d["pool"][torch.as_tensor(zero)], pool0[torch.as_tensor(zero)])
+    assert rel_l2(d["pool"][torch.as_tensor(used)], pool_ref[used]) <= tol
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_window_equals_single_steps(dtype):
+    """T = 1 windows through the slot table, repeated, equal one commit of the whole window
+    on the GPU, and the plain decode step on identity slots."""
+    import gated_deltanet_state_amd as g
+    N, T, H, D = 5, 4, 3, 128
+    say(f"decode_ex single steps dtype={dtype}")
+    inp = synth.make_serving(N, T, H, H, D, N, dtype, seed=5)
+    d = _cuda(inp)
+    a, b = d["pool"].clone(), d["pool"].clone()
+    o_win = g.gdn_decode_ex(a, d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], out_dtype=torch.float32)
+    steps = []
+    for t in range(T):
+        sl = lambda x: x[:, t:t + 1].contiguous()
+        steps.append(g.gdn_decode_ex(b, sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["beta"]), sl(d["log_alpha"]),
+                                     out_dtype=torch.float32))
+    c = d["pool"].clone()
+    o_step = [g.gdn_decode_step(c, d["q"][:, t].contiguous(), d["k"][:, t].contiguous(), d["v"][:, t].contiguous(),
+                                d["beta"][:, t].contiguous(), d["log_alpha"][:, t].contiguous(),
+                                out_dtype=torch.float32) for t in range(T)]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(o_win, torch.cat(steps, 1))
+    assert rel_l2(a, c) <= 1e-6 and rel_l2(o_win, torch.stack(o_step, 1)) <= 1e-6
+    o_ref, pool_ref = _ref(dict(inp, slots=torch.arange(N, dtype=torch.int32)), kda=False, raw=False,
+                           write_state=True, n_commit=False)
+    assert rel_l2(o_win, o_ref) <= 1e-5 and rel_l2(a, pool_ref) <= 1e-5
+
+
+def test_commit_zero_and_no_outputs():
+    import gated_deltanet_state_amd as g
+    N, T, H, D = 4, 2, 2, 32
+    inp = synth.make_serving(N, T, H, H, D, 8, torch.bfloat16, seed=9)
+    d = _cuda(inp)
+    pool0 = d["pool"].clone()
+    zeros = torch.zeros(N, dtype=torch.int32, device="cuda")
+    g.gdn_decode_commit(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], zeros, slots=d["slots"])
+    torch.cuda.synchronize()
+    assert torch.equal(d["pool"], pool0)
+
+
+def test_verify_workload_full_size_sampled():
+    """256 sequences x 32 value heads (16 query/key heads) x 128x128 states in a pool of 512,
+    4 draft tokens with the raw gate projections and unnormalised q, k: verification then
+    commit, checked on 12 sampled sequences (sequences are independent) and bit-exact for
+    every pool row no sequence addresses."""
+    import gated_deltanet_state_amd as g
+    c = synth.SERVING["verify"]
+    say("decode_ex verify workload: 256 x 32 heads, T=4, pool 512")
+    inp = synth.make_serving(c.N, c.T, c.H, c.Hqk, c.D, c.P, c.dtype, raw=True, s_std=c.s_std, seed=2001)
+    d = _cuda(inp)
+    kw = dict(slots=d["slots"], qk_l2norm=True, A_log=d["A_log"], dt_bias=d["dt_bias"])
+    pool0 = d["pool"].clone()
+    o = g.gdn_decode_verify(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], **kw)
+    g.gdn_decode_commit(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["n_commit"], **kw)
+    torch.cuda.synchronize()
+    pick = np.random.default_rng(0).choice(c.N, 12, replace=False)
+    sub = {k: (v[torch.as_tensor(pick)] if k in ("q", "k", "v", "beta", "log_alpha", "slots", "n_commit") else v)
+           for k, v in inp.items()}
+    rows = inp["slots"].numpy()[pick]
+    sub["pool"] = inp["pool"][torch.as_tensor(rows)]
+    sub["slots"] = torch.arange(len(pick), dtype=torch.int32)
+    o_ref, pool_ref = _ref(sub, kda=False, raw=True, write_state=True)
+    assert rel_l2(o[torch.as_tensor(pick)], o_ref) <= 2e-3
+    assert rel_l2(d["pool"][torch.as_tensor(rows)], pool_ref) <= 2e-3
+    unused = np.setdiff1d(np.arange(c.P), inp["slots"].numpy())
+    assert torch.equal(d["pool"][torch.as_tensor(unused)], pool0[torch.as_tensor(unused)])
