@@ -291,8 +291,8 @@ def main():
 
         ms_c = time_launches(commit, 20, 3, torch)
         nc = inp["n_commit"].numpy()
-        nb_c = int(cv.N * cv.H * state_b + (nc > 0).sum() * cv.H * state_b + nc.sum() * tok_in
-                   + 2 * cv.H * 4 + 2 * cv.N * 4)
+        # a sequence with no accepted token needs neither its state nor its inputs
+        nb_c = int(2 * (nc > 0).sum() * cv.H * state_b + nc.sum() * tok_in + 2 * cv.H * 4 + 2 * cv.N * 4)
         del d, o, inp
         torch.cuda.empty_cache()
         ck = synth.SERVING["kda"]
@@ -305,21 +305,24 @@ def main():
         nb_k = 2 * ck.N * ck.H * ck.D * ck.D * 4 + ck.N * (2 * ck.Hqk * ck.D + 2 * ck.H * ck.D + ck.H
                                                            + ck.H * ck.D) * 2
 
-        def rec(name, cfg, ms, nb, **more):
+        def rec(name, cfg, ms, nb, phase, **more):
             gb = nb / (ms * 1e-3) / 1e9
             r = {"workload": cfg.name, "N": cfg.N, "H": cfg.H, "H_qk": cfg.Hqk, "d": cfg.D, "T": cfg.T,
                  "pool_rows": cfg.P, "us": round(ms * 1e3, 2),
                  "roofline": {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": round(gb / HBM_PEAK_GBS, 4), "traffic": None,
+                              "frac": round(gb / HBM_PEAK_GBS, 4),
+                              "traffic": _traffic(f"decode_ex_{phase}", ["gdn_decode.hip"]),
                               "kernel": "decode_ex_kernel", "algorithmic_bytes": int(nb)}}
             r.update(more)
             log(f"serving {name}: {ms * 1e3:.1f} us, {gb:.0f} GB/s, HBM frac {gb / HBM_PEAK_GBS:.3f}")
             return r
 
         extra["serving_decode"] = {
-            "verify": rec("verify", cv, ms_v, nb_v, draft_tokens=cv.T, fused="q/k L2 norm, gate activations"),
-            "commit": rec("commit", cv, ms_c, nb_c, accepted_tokens=int(nc.sum())),
-            "kda_step": rec("kda step", ck, ms_k, nb_k),
+            "verify": rec("verify", cv, ms_v, nb_v, "verify", draft_tokens=cv.T,
+                          fused="q/k L2 norm, gate activations"),
+            "commit": rec("commit", cv, ms_c, nb_c, "commit", accepted_tokens=int(nc.sum()),
+                          sequences_committing=int((nc > 0).sum())),
+            "kda_step": rec("kda step", ck, ms_k, nb_k, "kda_step"),
         }
         del d, o, inp
         torch.cuda.empty_cache()
