@@ -20,7 +20,7 @@ __all__ = [
     "gdn_status_string", "gdn_version", "library_path", "lib",
     "GDN_F32", "GDN_BF16", "GDN_SUCCESS", "GDN_ERROR_INVALID_VALUE", "GDN_ERROR_NOT_SUPPORTED",
     "GDN_ERROR_HIP", "GdnChunkDesc", "GdnDecodeExDesc", "gdn_decode_ex", "gdn_decode_verify",
-    "gdn_decode_commit",
+    "gdn_decode_commit", "GdnChunkExDesc", "gdn_chunk_fwd_ex",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +38,12 @@ class GdnChunkDesc(ctypes.Structure):
         ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
         ("ckpt_every", ctypes.c_int64),
     ]
+
+
+class GdnChunkExDesc(ctypes.Structure):
+    """Mirror of gdn_chunk_ex_desc_t."""
+    _fields_ = [("base", GdnChunkDesc), ("H_qk", ctypes.c_int64), ("raw_gates", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class GdnDecodeExDesc(ctypes.Structure):
@@ -73,6 +79,8 @@ def _load() -> ctypes.CDLL:
         f.restype = ci
     L.gdn_decode_step.argtypes = [i64, i64, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gdn_decode_step.restype = ci
+    L.gdn_chunk_fwd_ex.argtypes = [ctypes.POINTER(GdnChunkExDesc)] + [vp] * 12
+    L.gdn_chunk_fwd_ex.restype = ci
     L.gdn_decode_ex.argtypes = [ctypes.POINTER(GdnDecodeExDesc)] + [vp] * 12
     L.gdn_decode_ex.restype = ci
     L.gdn_status_string.argtypes = [ci]
@@ -278,3 +286,54 @@ def gdn_decode_commit(pool, q, k, v, beta, log_alpha, n_commit, **kw):
     """Apply the first n_commit[n] tokens of each window to the pool rows in place."""
     kw.setdefault("return_o", False)
     return gdn_decode_ex(pool, q, k, v, beta, log_alpha, n_commit=n_commit, write_state=True, **kw)
+
+
+def gdn_chunk_fwd_ex(q, k, v, beta, log_alpha, s0=None, *, A_log=None, dt_bias=None, chunk: int = 64,
+                     ckpt_every: int = 0, out_dtype=None, o=None, s_final=None, s_ckpt=None,
+                     return_final: bool = True, stream=None):
+    """Chunkwise prefill with grouped query/key heads and optionally the raw gate projections
+    (gdn_chunk_fwd_ex in include/gdn.h).
+
+    q, k [B,Hqk,T,D]; v [B,H,T,D]; beta, log_alpha [B,H,T] (b and a when A_log, dt_bias [H]
+    fp32 are given); s0 [B,H,D,D] fp32 or None.  Returns (o, s_final, s_ckpt) like
+    gdn_chunk_fwd.
+    """
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B, Hqk, T, D] and v [B, H, T, D]")
+    B, Hqk, T, D = q.shape
+    H = v.shape[1]
+    dev, in_dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    out_dt = out_dtype or in_dt
+    _check(k, "k", (B, Hqk, T, D), in_dt, dev)
+    _check(v, "v", (B, H, T, D), in_dt, dev)
+    _check(beta, "beta", (B, H, T), in_dt, dev)
+    _check(log_alpha, "log_alpha", (B, H, T), in_dt, dev)
+    raw = A_log is not None
+    if raw:
+        _check(A_log, "A_log", (H,), torch.float32, dev)
+        _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    if s0 is not None:
+        _check(s0, "s0", (B, H, D, D), torch.float32, dev)
+    if o is None:
+        o = torch.empty(B, H, T, D, dtype=out_dt, device=dev)
+    _check(o, "o", (B, H, T, D), out_dt, dev)
+    if s_final is None and return_final:
+        s_final = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    if s_final is not None:
+        _check(s_final, "s_final", (B, H, D, D), torch.float32, dev)
+    n_ck = T // ckpt_every if ckpt_every > 0 else 0
+    if n_ck > 0:
+        if s_ckpt is None:
+            s_ckpt = torch.empty(B, H, n_ck, D, D, dtype=torch.float32, device=dev)
+        _check(s_ckpt, "s_ckpt", (B, H, n_ck, D, D), torch.float32, dev)
+    else:
+        s_ckpt = None
+    d = GdnChunkExDesc(_desc(B, H, T, D, chunk, in_dt, out_dt, ckpt_every), Hqk, int(raw), 0)
+    st = lib.gdn_chunk_fwd_ex(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                              _ptr(A_log), _ptr(dt_bias), _ptr(s0), _ptr(o), _ptr(s_final), _ptr(s_ckpt),
+                              _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GdnError(st, "gdn_chunk_fwd_ex")
+    return o, s_final, s_ckpt

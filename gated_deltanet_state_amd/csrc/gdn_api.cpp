@@ -49,19 +49,40 @@ gdn_status_t check_chunk_desc(const gdn_chunk_desc_t* d, int is_kda, gdn::ChunkA
   a.B = d->B; a.H = d->H; a.T = d->T; a.D = d->Dk; a.chunk = d->chunk;
   a.in_dtype = d->in_dtype; a.out_dtype = d->out_dtype; a.ckpt_every = d->ckpt_every;
   a.n_ckpt = d->ckpt_every > 0 ? d->T / d->ckpt_every : 0;
+  a.Hqk = d->H;  // one query/key head per value head unless gdn_chunk_fwd_ex says otherwise
   (void)is_kda;
   if (!gdn::chunk_mfma_supported(a) && !gdn::chunk_valu_supported(a)) return GDN_ERROR_NOT_SUPPORTED;
   *out = a;
   return GDN_SUCCESS;
 }
 
+// Layer prologue of gdn_chunk_fwd_ex (NULL for the plain entry points).
+struct Prologue {
+  int64_t H_qk;
+  int raw_gates;
+  const float *A_log, *dt_bias;
+};
+
 gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, const void* k,
                        const void* v, const void* beta, const void* log_alpha, const float* s0,
                        void* o, float* s_final, float* s_ckpt, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, void* stream, const Prologue* pro = nullptr) {
   gdn::ChunkArgs a;
   gdn_status_t st = check_chunk_desc(d, is_kda, &a);
   if (st != GDN_SUCCESS) return st;
+  if (pro) {
+    if (pro->H_qk <= 0 || a.H % pro->H_qk != 0) return GDN_ERROR_INVALID_VALUE;
+    if (pro->raw_gates != 0 && pro->raw_gates != 1) return GDN_ERROR_INVALID_VALUE;
+    // the prologue runs in the matrix-core kernel only; without one, the plain paths apply
+    if ((pro->H_qk != a.H || pro->raw_gates) && !gdn::chunk_mfma_supported(a)) return GDN_ERROR_NOT_SUPPORTED;
+    if (pro->raw_gates && (!pro->A_log || !pro->dt_bias || !aligned_elem(pro->A_log, GDN_F32) ||
+                           !aligned_elem(pro->dt_bias, GDN_F32)))
+      return GDN_ERROR_INVALID_VALUE;
+    a.Hqk = pro->H_qk;
+    a.raw_gates = pro->raw_gates;
+    a.A_log = pro->raw_gates ? pro->A_log : nullptr;
+    a.dt_bias = pro->raw_gates ? pro->dt_bias : nullptr;
+  }
   (void)workspace;
   (void)workspace_bytes;  // the fused kernels need no workspace (size 0)
   const int64_t BH = a.B * a.H;
@@ -134,6 +155,15 @@ gdn_status_t kda_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void*
                            void* stream) {
   return chunk_fwd(1, d, q, k, v, beta, log_alpha, s0, o, s_final, s_ckpt, workspace,
                    workspace_bytes, stream);
+}
+
+gdn_status_t gdn_chunk_fwd_ex(const gdn_chunk_ex_desc_t* d, const void* q, const void* k, const void* v,
+                              const void* beta, const void* log_alpha, const float* A_log,
+                              const float* dt_bias, const float* s0, void* o, float* s_final,
+                              float* s_ckpt, void* stream) {
+  if (!d || d->reserved != 0) return GDN_ERROR_INVALID_VALUE;
+  const Prologue pro = {d->H_qk, d->raw_gates, A_log, dt_bias};
+  return chunk_fwd(0, &d->base, q, k, v, beta, log_alpha, s0, o, s_final, s_ckpt, nullptr, 0, stream, &pro);
 }
 
 gdn_status_t gdn_decode_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv, gdn_dtype_t in_dtype,

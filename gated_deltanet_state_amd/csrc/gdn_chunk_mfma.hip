@@ -536,9 +536,9 @@ __device__ __forceinline__ void toff_part(Smem& sm, int64_t c, int l) {
 // previous phase 2), and part COLS = half of the off-diagonal blocks of T for chunk c + 1
 // (phase 2).
 template <int half>
-__device__ __forceinline__ void key_toff_role(Smem& sm, const ChunkArgs& p, int64_t bh, int l, int64_t nchunks) {
+__device__ __forceinline__ void key_toff_role(Smem& sm, const ChunkArgs& p, int64_t bhq, int l, int64_t nchunks) {
   // two register sets: each chunk's rows are loaded two iterations before they are stored
-  RowStage<half> ka(p.k, p, bh, l), kb(p.k, p, bh, l);
+  RowStage<half> ka(p.k, p, bhq, l), kb(p.k, p, bhq, l);
   ka.load(0);
   kb.load(C);
   auto iter = [&](int c, RowStage<half>& ks) {
@@ -558,7 +558,8 @@ __device__ __forceinline__ void key_toff_role(Smem& sm, const ChunkArgs& p, int6
 // Role: gate tables of chunk c + 2 (wave 8, phase 1; their buffer last held chunk c - 1), and the
 // second half of the queries and the value slice of chunk c + 1 (phase 2; every reader of those
 // buffers runs in phase 1).
-__device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int64_t bh, int c0, int l,
+template <bool RAW>
+__device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int64_t bh, int64_t bhq, int c0, int l,
                                               int64_t nchunks) {
   const int64_t tok0 = bh * p.T;
   const auto br = stream_rsrc(p.beta, tok0, p.T);
@@ -571,7 +572,7 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int6
     uint32_t bb, gg;
     v4u vv[4];
   };
-  RowStage<1> qa(p.q, p, bh, l), qb(p.q, p, bh, l);
+  RowStage<1> qa(p.q, p, bhq, l), qb(p.q, p, bhq, l);
   Set sa, sb;
   auto load_g = [&](Set& st, int64_t t0) {
     st.bb = __builtin_amdgcn_raw_buffer_load_b16(br, (int)((t0 + l) * 2), 0, 0);
@@ -589,14 +590,29 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int6
   load_v(sa, -C);
   qb.load(0);
   load_v(sb, 0);
+  // raw gate projections (layer prologue): beta = sigmoid(b), log alpha = -exp(A_log) softplus(a + dt_bias)
+  float Aexp = 0.f, dtb = 0.f;
+  if constexpr (RAW) {
+    const int64_t h = bh % p.H;
+    Aexp = __expf(p.A_log[h]);
+    dtb = p.dt_bias[h];
+  }
   auto iter = [&](int c, Set& st, RowStage<1>& qs) {
     {
-      const float x = wave_prefix_sum(bf16_bits_to_f32(st.gg & 0xffffu));
+      float g = bf16_bits_to_f32(st.gg & 0xffffu), bt = bf16_bits_to_f32(st.bb & 0xffffu);
+      if constexpr (RAW) {
+        // tokens past the end read as b = a = 0; they must stay identity steps
+        const bool live = (int64_t)(c + 2) * C + l < p.T;
+        const float xa = g + dtb;
+        g = live ? -Aexp * (fmaxf(xa, 0.f) + log1pf(__expf(-fabsf(xa)))) : 0.f;
+        bt = live ? 1.f / (1.f + __expf(-bt)) : 0.f;
+      }
+      const float x = wave_prefix_sum(g);
       const float glast = __shfl(x, C - 1, 64);
       const float gr1 = __shfl(x, 15, 64), gr2 = __shfl(x, 31, 64), gr3 = __shfl(x, 47, 64);
       const int R = l >> 4;
       const float gref = R == 0 ? 0.f : (R == 1 ? gr1 : (R == 2 ? gr2 : gr3));
-      const float beta = bf16_bits_to_f32(st.bb & 0xffffu);
+      const float beta = bt;
       Gates& gt = sm.gt[kbuf(c + 2)];
       const float gam = __expf(x), el = __expf(x - gref);
       gt.G[l] = x;
@@ -633,8 +649,8 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int6
 }
 
 // Role: first half of the queries of chunk c + 1 (wave 9, phase 2), loaded two iterations ahead.
-__device__ __forceinline__ void q_role(Smem& sm, const ChunkArgs& p, int64_t bh, int l, int64_t nchunks) {
-  RowStage<0> qa(p.q, p, bh, l), qb(p.q, p, bh, l);
+__device__ __forceinline__ void q_role(Smem& sm, const ChunkArgs& p, int64_t bhq, int l, int64_t nchunks) {
+  RowStage<0> qa(p.q, p, bhq, l), qb(p.q, p, bhq, l);
   qa.load(-C);
   qb.load(0);
   auto iter = [&](int c, RowStage<0>& qs) {
@@ -730,7 +746,7 @@ __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
   }
 }
 
-template <typename TOut>
+template <typename TOut, bool RAW>
 __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
@@ -744,6 +760,8 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
   if (nblk % (8 * NT) == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
   const int c0 = (int)(bid % NT) * DVT;
   const int64_t bh = bid / NT;
+  // value head h of batch b reads query/key head h / (H / Hqk)
+  const int64_t bhq = (bh / p.H) * p.Hqk + (bh % p.H) / (p.H / p.Hqk);
   const int64_t nchunks = (p.T + C - 1) / C;
 
   // T and P start at zero; their upper blocks are never written
@@ -763,10 +781,10 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
     case 3: tdiag_role<2>(sm, l, nchunks); break;
     case 4: out_role<TOut, 0>(sm, p, bh, c0, l, nchunks); break;
     case 5: out_role<TOut, 2>(sm, p, bh, c0, l, nchunks); break;
-    case 6: key_toff_role<0>(sm, p, bh, l, nchunks); break;
-    case 7: key_toff_role<1>(sm, p, bh, l, nchunks); break;
-    case 8: gates_qv_role(sm, p, bh, c0, l, nchunks); break;
-    case 9: q_role(sm, p, bh, l, nchunks); break;
+    case 6: key_toff_role<0>(sm, p, bhq, l, nchunks); break;
+    case 7: key_toff_role<1>(sm, p, bhq, l, nchunks); break;
+    case 8: gates_qv_role<RAW>(sm, p, bh, bhq, c0, l, nchunks); break;
+    case 9: q_role(sm, p, bhq, l, nchunks); break;
     case 10: pa_role<0>(sm, l, nchunks); break;
     default: pa_role<1>(sm, l, nchunks); break;
   }
@@ -783,10 +801,14 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a, bool kda, hipStream_t s) {
   if (kda) return launch_kda_mfma(a, s);
   const int64_t blocks = a.B * a.H * NT;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (a.out_dtype == GDN_BF16)
-    hipLaunchKernelGGL((gdn_chunk_mfma_kernel<__hip_bfloat16>), dim3((unsigned)blocks), dim3(NTH), 0, s, a);
-  else
-    hipLaunchKernelGGL((gdn_chunk_mfma_kernel<float>), dim3((unsigned)blocks), dim3(NTH), 0, s, a);
+  const dim3 grid((unsigned)blocks), block(NTH);
+  if (a.out_dtype == GDN_BF16) {
+    if (a.raw_gates) hipLaunchKernelGGL((gdn_chunk_mfma_kernel<__hip_bfloat16, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gdn_chunk_mfma_kernel<__hip_bfloat16, false>), grid, block, 0, s, a);
+  } else {
+    if (a.raw_gates) hipLaunchKernelGGL((gdn_chunk_mfma_kernel<float, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gdn_chunk_mfma_kernel<float, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

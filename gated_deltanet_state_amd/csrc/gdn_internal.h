@@ -21,6 +21,10 @@ struct ChunkArgs {
   void* o;
   float* s_final;          // may be null
   float* s_ckpt;           // may be null iff n_ckpt == 0
+  // layer prologue (gdn_chunk_fwd_ex; matrix-core path only)
+  int64_t Hqk;             // query/key heads (H a multiple); equals H for the plain entry points
+  int raw_gates;           // beta / log_alpha carry the raw b / a projections
+  const float *A_log, *dt_bias;  // [H], raw gates only
 };
 
 struct DecodeArgs {

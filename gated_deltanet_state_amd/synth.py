@@ -180,3 +180,26 @@ def make_serving(N: int, T: int, H: int, Hqk: int, D: int, P: int, dtype: torch.
     return {"pool": pool, "slots": slots, "n_commit": n_commit, "q": q.to(dtype), "k": k.to(dtype),
             "v": v.to(dtype), "beta": beta.to(dtype), "log_alpha": log_alpha.to(dtype),
             "A_log": A_log, "dt_bias": dt_bias}
+
+
+def make_prefill_ex(B: int, H: int, Hqk: int, T: int, D: int, dtype: torch.dtype = torch.bfloat16, *,
+                    raw: bool = False, s0_std: float = 0.01, seed: int = 0) -> Dict[str, Optional[torch.Tensor]]:
+    """Prefill inputs with H value heads reading Hqk query/key heads, drawn in the order q, k,
+    v, gates, s0 (and A_log, dt_bias for raw gates): q, k [B, Hqk, T, D] of unit length,
+    v [B, H, T, D]; the gates as in ``make_serving``."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = _unit(torch.randn(B, Hqk, T, D, generator=g))
+    k = _unit(torch.randn(B, Hqk, T, D, generator=g))
+    v = torch.randn(B, H, T, D, generator=g)
+    A_log = dt_bias = None
+    if raw:
+        beta = torch.randn(B, H, T, generator=g)
+        log_alpha = torch.randn(B, H, T, generator=g)
+        A_log = torch.rand(H, generator=g) * 2 - 1
+        dt_bias = torch.rand(H, generator=g) * 2 - 4
+    else:
+        beta = torch.sigmoid(torch.randn(B, H, T, generator=g))
+        log_alpha = torch.rand(B, H, T, generator=g) * 0.195 - 0.2
+    s0 = (torch.randn(B, H, D, D, generator=g) * s0_std) if s0_std > 0 else None
+    return {"q": q.to(dtype), "k": k.to(dtype), "v": v.to(dtype), "beta": beta.to(dtype),
+            "log_alpha": log_alpha.to(dtype), "s0": s0, "A_log": A_log, "dt_bias": dt_bias}

@@ -125,6 +125,35 @@ gdn_status_t kda_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void*
                            void* stream);
 
 /*
+ * Chunkwise prefill of the gated delta rule with parts of the layer around the core fused
+ * in (gdn_chunk_fwd otherwise):
+ *  - value heads sharing query/key heads: base.H value heads, H_qk query/key heads (base.H
+ *    a multiple of H_qk); value head h reads query/key head h / (base.H / H_qk);
+ *  - raw_gates = 1: beta and log_alpha carry the layer's raw projections b and a, and the
+ *    kernel forms beta = sigmoid(b), log alpha = -exp(A_log) softplus(a + dt_bias)
+ *    ("Attention, Part 4", section "Where alpha and beta come from").
+ *
+ *   q, k      [B, H_qk, T, Dk]   in_dtype
+ *   v         [B, H, T, Dv]; beta, log_alpha [B, H, T]; s0, o, s_final, s_ckpt as in
+ *             gdn_chunk_fwd
+ *   A_log, dt_bias [H] fp32, required when raw_gates = 1, ignored otherwise
+ * Supported on the matrix-core path (bf16 inputs, Dk = Dv = 128, chunk = 64); with
+ * H_qk = H and raw_gates = 0 every combination gdn_chunk_fwd supports.  q and k are used
+ * as given: normalise them before the call.  `reserved` must be 0.
+ */
+typedef struct {
+  gdn_chunk_desc_t base;
+  int64_t H_qk;
+  int32_t raw_gates;
+  int32_t reserved;
+} gdn_chunk_ex_desc_t;
+
+gdn_status_t gdn_chunk_fwd_ex(const gdn_chunk_ex_desc_t* d, const void* q, const void* k, const void* v,
+                              const void* beta, const void* log_alpha, const float* A_log,
+                              const float* dt_bias, const float* s0, void* o, float* s_final,
+                              float* s_ckpt, void* stream);
+
+/*
  * One recurrent (decode) step of the gated delta rule for every live sequence: each
  * sequence keeps a fixed-size state that is updated in place once per token
  * ("From Traditional Attention to hybrid ones", section "vLLM Storage": the state is

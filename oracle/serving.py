@@ -9,6 +9,8 @@ Everything here is a plain composition of pinned pieces:
   * ``gates_from_raw``   -- beta and log alpha from the raw per-head projections.
                             Pinned by closed forms (sigmoid(0) = 1/2, softplus(0) = ln 2,
                             softplus(ln(e - 1)) = 1, limits, sign of log alpha).
+  * ``forward_ex``       -- the prefill with grouped query/key heads and raw gates: the
+                            pinned ``oracle.forward`` on repeated heads and gates_from_raw.
   * ``decode_window``    -- T tokens per sequence on slot-addressed states, each token one
                             call of the pinned single-token step (``oracle.decode_step``).
                             Pinned against the independent token loop of ``oracle.forward``
@@ -131,3 +133,28 @@ def widen_int(x) -> np.ndarray:
     except ImportError:  # pragma: no cover
         pass
     return np.asarray(x).astype(np.int64)
+
+
+def forward_ex(q, k, v, beta, log_alpha, s0=None, *, raw_gates: bool = False, A_log=None, dt_bias=None,
+               ckpt_every: int = 0):
+    """The token-loop forward pass (``oracle.forward``) with H value heads reading
+    Hqk = q.shape[1] query/key heads (value head h reads head h // (H / Hqk)), and with the
+    raw gate projections b, a turned into beta and log alpha by ``gates_from_raw`` when
+    ``raw_gates``.  q, k [B, Hqk, T, Dk]; v [B, H, T, Dv]; beta, log_alpha [B, H, T] (b, a for
+    raw gates; A_log, dt_bias [H]).  Returns (o, s_final, s_ckpt) in fp64."""
+    from . import forward
+    q, k, v = widen(q), widen(k), widen(v)
+    B, Hqk, T, Dk = q.shape
+    H = v.shape[1]
+    if H % Hqk != 0:
+        raise ValueError("oracle: H must be a multiple of Hqk")
+    G = H // Hqk
+    q, k = np.repeat(q, G, axis=1), np.repeat(k, G, axis=1)
+    if raw_gates:
+        beta, log_alpha = gates_from_raw(np.moveaxis(widen(beta), 1, -1), np.moveaxis(widen(log_alpha), 1, -1),
+                                         A_log, dt_bias)
+        beta, log_alpha = np.moveaxis(beta, -1, 1).copy(), np.moveaxis(log_alpha, -1, 1).copy()
+    else:
+        beta, log_alpha = widen(beta), widen(log_alpha)
+    s0 = None if s0 is None else widen(s0)
+    return forward(q, k, v, beta, log_alpha, s0, ckpt_every=ckpt_every)

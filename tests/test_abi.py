@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
-        "gdn_chunk_fwd", "gdn_chunk_workspace_size", "gdn_decode_ex", "gdn_decode_step",
+        "gdn_chunk_fwd", "gdn_chunk_fwd_ex", "gdn_chunk_workspace_size", "gdn_decode_ex", "gdn_decode_step",
         "gdn_status_string", "gdn_version", "kda_chunk_fwd"])
 
 
@@ -38,6 +38,7 @@ def test_desc_struct_layout(g):
     assert ctypes.sizeof(g.GdnChunkDesc) == 64
     assert g.GdnChunkDesc.ckpt_every.offset == 56
     assert ctypes.sizeof(g.GdnDecodeExDesc) == 80
+    assert ctypes.sizeof(g.GdnChunkExDesc) == 80 and g.GdnChunkExDesc.raw_gates.offset == 72
     assert g.GdnDecodeExDesc.in_dtype.offset == 56 and g.GdnDecodeExDesc.write_state.offset == 76
 
 
@@ -162,3 +163,28 @@ def test_decode_ex_validation_errors(g):
     assert _ex_call(g, _ex_desc(g, N=0)) == OK
     assert _ex_call(g, _ex_desc(g, P=0)) == OK
     assert _ex_call(g, _ex_desc(g, write_state=0), o=None) == OK
+
+
+def test_chunk_ex_validation_errors(g):
+    INV, NS, OK = g.GDN_ERROR_INVALID_VALUE, g.GDN_ERROR_NOT_SUPPORTED, g.GDN_SUCCESS
+    f = g.lib.gdn_chunk_fwd_ex
+    p = [ctypes.c_void_p(FAKE + i * 0x1000000) for i in range(11)]
+
+    def call(d, **kw):
+        q = list(p)
+        for i, val in kw.items():
+            q[int(i[1:])] = val
+        return f(None if d is None else ctypes.byref(d), *q, None)
+
+    def ex(h_qk=2, raw=0, reserved=0, **kw):
+        return g.GdnChunkExDesc(_desc(g, H=4, **kw), h_qk, raw, reserved)
+
+    assert call(None) == INV
+    assert call(ex(reserved=1)) == INV
+    assert call(ex(h_qk=3)) == INV                        # H = 4 not a multiple of 3
+    assert call(ex(h_qk=0)) == INV
+    assert call(ex(raw=2)) == INV
+    assert call(ex(raw=1), a5=None) == INV                # A_log missing
+    assert call(ex(in_dtype=g.GDN_F32)) == NS             # grouped heads: matrix-core path only
+    assert call(ex(h_qk=4, in_dtype=g.GDN_F32, Dk=16, Dv=16, chunk=16)) != NS   # plain: vector path
+    assert call(ex(B=0)) == OK

@@ -160,3 +160,24 @@ def test_fused_prologue_composes():
     beta, la = serving.gates_from_raw(b, a, A_log, dt)
     o2 = serving.decode_window(p2, serving.l2_normalize(q), serving.l2_normalize(k), v, beta, la)
     assert np.array_equal(o1, o2) and np.array_equal(p1, p2)
+
+
+def test_forward_ex_matches_decode_windows():
+    """The prefill with grouped heads and raw gates (ora_forward underneath) equals the same
+    tokens run as decode windows (ora_decode_step underneath)."""
+    rng = np.random.default_rng(7)
+    B, Hqk, H, T, D = 2, 2, 4, 9, 8
+    q = rng.normal(0, 1, (B, Hqk, T, D))
+    k = rng.normal(0, 1, (B, Hqk, T, D))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.normal(0, 1, (B, H, T, D))
+    b, a = rng.normal(0, 1, (B, H, T)), rng.normal(0, 1, (B, H, T))
+    A_log, dt = rng.normal(-1, 0.5, H), rng.normal(0, 0.5, H)
+    s0 = rng.normal(0, 0.1, (B, H, D, D))
+    o, sf, _ = serving.forward_ex(q, k, v, b, a, s0, raw_gates=True, A_log=A_log, dt_bias=dt)
+    pool = s0.copy()
+    ow = serving.decode_window(pool, q.transpose(0, 2, 1, 3), k.transpose(0, 2, 1, 3), v.transpose(0, 2, 1, 3),
+                               b.transpose(0, 2, 1), a.transpose(0, 2, 1), raw_gates=True, A_log=A_log, dt_bias=dt)
+    assert np.allclose(o, ow.transpose(0, 2, 1, 3), rtol=0, atol=1e-13)
+    assert np.allclose(sf, pool, rtol=0, atol=1e-13)
