@@ -15,6 +15,8 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+
+import numpy as np
 import json
 import os
 import sys
@@ -295,6 +297,32 @@ def main():
             "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         log(f"prefill_ex: {ms * 1e3:.1f} us, {gb:.0f} GB/s")
         del d, o, sf
+        torch.cuda.empty_cache()
+
+    # ---------------- ragged prefill: 16 prompts of 256..1792 tokens in one call ----------------
+    if args.only in ("prefill_ex", "all"):
+        H, D = 16, 128
+        lens = synth.ragged_lengths(16, 256, 1792, seed=2004)
+        seqs = [synth.make_prefill(1, H, n, D, D, seed=3000 + i) for i, n in enumerate(lens)]
+        pk = lambda key: torch.cat([x[key][0].reshape(H * x[key].shape[2], *x[key].shape[3:]) for x in seqs], 0).to(dev)
+        d = {key: pk(key) for key in ("q", "k", "v", "beta", "log_alpha")}
+        s0 = torch.cat([x["s0"] for x in seqs], 0).to(dev)
+        cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
+        del seqs
+        T = int(sum(lens))
+        ms = time_launches(lambda i: g.gdn_chunk_fwd_ragged(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], cu,
+                                                            H=H, s0=s0), 20, 3, torch)
+        nb = H * T * ((3 * D + 2) * 2 + D * 2) + 2 * len(lens) * H * D * D * 4
+        gb = nb / (ms * 1e-3) / 1e9
+        extra["prefill_ragged"] = {
+            "workload": "gdn_prefill_ragged16_bf16", "sequences": len(lens), "tokens": T, "H": H, "d": D,
+            "lengths": f"uniform 256..1792 (seeded), min {min(lens)}, max {max(lens)}",
+            "us": round(ms * 1e3, 2), "Mtok_per_s": round(T / (ms * 1e-3) / 1e6, 3),
+            "roofline": {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gb / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "gdn_chunk_mfma_kernel", "algorithmic_bytes": int(nb)}}
+        log(f"prefill_ragged: {T} tokens in {ms * 1e3:.1f} us, {T / (ms * 1e-3) / 1e6:.1f} Mtok/s")
+        del d, s0, cu
         torch.cuda.empty_cache()
 
     # ---------------- serving-side decode windows: verify 4 draft tokens, commit, KDA step ----------------

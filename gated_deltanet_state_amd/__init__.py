@@ -20,7 +20,8 @@ __all__ = [
     "gdn_status_string", "gdn_version", "library_path", "lib",
     "GDN_F32", "GDN_BF16", "GDN_SUCCESS", "GDN_ERROR_INVALID_VALUE", "GDN_ERROR_NOT_SUPPORTED",
     "GDN_ERROR_HIP", "GdnChunkDesc", "GdnDecodeExDesc", "gdn_decode_ex", "gdn_decode_verify",
-    "gdn_decode_commit", "GdnChunkExDesc", "gdn_chunk_fwd_ex",
+    "gdn_decode_commit", "GdnChunkExDesc", "gdn_chunk_fwd_ex", "gdn_chunk_fwd_ragged", "pack_ragged",
+    "unpack_ragged",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,7 +80,7 @@ def _load() -> ctypes.CDLL:
         f.restype = ci
     L.gdn_decode_step.argtypes = [i64, i64, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gdn_decode_step.restype = ci
-    L.gdn_chunk_fwd_ex.argtypes = [ctypes.POINTER(GdnChunkExDesc)] + [vp] * 12
+    L.gdn_chunk_fwd_ex.argtypes = [ctypes.POINTER(GdnChunkExDesc)] + [vp] * 13
     L.gdn_chunk_fwd_ex.restype = ci
     L.gdn_decode_ex.argtypes = [ctypes.POINTER(GdnDecodeExDesc)] + [vp] * 12
     L.gdn_decode_ex.restype = ci
@@ -332,8 +333,74 @@ def gdn_chunk_fwd_ex(q, k, v, beta, log_alpha, s0=None, *, A_log=None, dt_bias=N
         s_ckpt = None
     d = GdnChunkExDesc(_desc(B, H, T, D, chunk, in_dt, out_dt, ckpt_every), Hqk, int(raw), 0)
     st = lib.gdn_chunk_fwd_ex(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
-                              _ptr(A_log), _ptr(dt_bias), _ptr(s0), _ptr(o), _ptr(s_final), _ptr(s_ckpt),
+                              _ptr(A_log), _ptr(dt_bias), None, _ptr(s0), _ptr(o), _ptr(s_final), _ptr(s_ckpt),
                               _stream(stream))
     if st != GDN_SUCCESS:
         raise GdnError(st, "gdn_chunk_fwd_ex")
     return o, s_final, s_ckpt
+
+
+def pack_ragged(seqs):
+    """Concatenate per-sequence tensors [heads, T_b, ...] into the packed [heads * sum T_b, ...]
+    layout of a ragged batch; returns (packed, cu_seqlens as an int32 list)."""
+    cu = [0]
+    for x in seqs:
+        cu.append(cu[-1] + int(x.shape[1]))
+    flat = [x.reshape(x.shape[0] * x.shape[1], *x.shape[2:]) for x in seqs]
+    return torch.cat(flat, 0), cu
+
+
+def unpack_ragged(packed, cu, heads: int):
+    """Inverse of pack_ragged: a list of [heads, T_b, ...] views."""
+    out = []
+    for b in range(len(cu) - 1):
+        t0, t1 = cu[b], cu[b + 1]
+        out.append(packed[heads * t0:heads * t1].reshape(heads, t1 - t0, *packed.shape[1:]))
+    return out
+
+
+def gdn_chunk_fwd_ragged(q, k, v, beta, log_alpha, cu_seqlens, *, H: int, H_qk: int = None, s0=None,
+                         A_log=None, dt_bias=None, out_dtype=None, o=None, s_final=None,
+                         return_final: bool = True, stream=None):
+    """Prefill of a ragged batch (gdn_chunk_fwd_ex with cu_seqlens): B sequences of different
+    lengths in one call.
+
+    cu_seqlens: int32 [B + 1] on the device (0 = cu[0] <= ... <= cu[B] = T).  Packed tensors
+    (see pack_ragged): q, k [H_qk * T, D]; v [H * T, D]; beta, log_alpha [H * T]; s0, s_final
+    [B, H, D, D] fp32.  Returns (o [H * T, D], s_final)."""
+    H_qk = H if H_qk is None else H_qk
+    if q.dim() != 2 or cu_seqlens.dim() != 1:
+        raise ValueError("q must be [H_qk * T, D] and cu_seqlens [B + 1]")
+    if H <= 0 or H_qk <= 0 or q.shape[0] % H_qk:
+        raise ValueError("q rows must be a multiple of H_qk")
+    T, D = q.shape[0] // H_qk, q.shape[1]
+    B = cu_seqlens.shape[0] - 1
+    dev, in_dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    out_dt = out_dtype or in_dt
+    _check(k, "k", (H_qk * T, D), in_dt, dev)
+    _check(v, "v", (H * T, D), in_dt, dev)
+    _check(beta, "beta", (H * T,), in_dt, dev)
+    _check(log_alpha, "log_alpha", (H * T,), in_dt, dev)
+    _check(cu_seqlens, "cu_seqlens", (B + 1,), torch.int32, dev)
+    raw = A_log is not None
+    if raw:
+        _check(A_log, "A_log", (H,), torch.float32, dev)
+        _check(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    if s0 is not None:
+        _check(s0, "s0", (B, H, D, D), torch.float32, dev)
+    if o is None:
+        o = torch.empty(H * T, D, dtype=out_dt, device=dev)
+    _check(o, "o", (H * T, D), out_dt, dev)
+    if s_final is None and return_final:
+        s_final = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    if s_final is not None:
+        _check(s_final, "s_final", (B, H, D, D), torch.float32, dev)
+    d = GdnChunkExDesc(_desc(B, H, T, D, 64, in_dt, out_dt, 0), H_qk, int(raw), 0)
+    st = lib.gdn_chunk_fwd_ex(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                              _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(s0), _ptr(o), _ptr(s_final),
+                              None, _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GdnError(st, "gdn_chunk_fwd_ex")
+    return o, s_final

@@ -61,6 +61,7 @@ struct Prologue {
   int64_t H_qk;
   int raw_gates;
   const float *A_log, *dt_bias;
+  const int32_t* cu_seqlens;  // ragged batch: [B + 1] token offsets, T = total tokens
 };
 
 gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, const void* k,
@@ -74,7 +75,13 @@ gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, con
     if (pro->H_qk <= 0 || a.H % pro->H_qk != 0) return GDN_ERROR_INVALID_VALUE;
     if (pro->raw_gates != 0 && pro->raw_gates != 1) return GDN_ERROR_INVALID_VALUE;
     // the prologue runs in the matrix-core kernel only; without one, the plain paths apply
-    if ((pro->H_qk != a.H || pro->raw_gates) && !gdn::chunk_mfma_supported(a)) return GDN_ERROR_NOT_SUPPORTED;
+    if ((pro->H_qk != a.H || pro->raw_gates || pro->cu_seqlens) && !gdn::chunk_mfma_supported(a))
+      return GDN_ERROR_NOT_SUPPORTED;
+    if (pro->cu_seqlens) {
+      if (a.ckpt_every != 0) return GDN_ERROR_NOT_SUPPORTED;  // snapshots need a common length
+      if (!aligned_elem(pro->cu_seqlens, GDN_F32)) return GDN_ERROR_INVALID_VALUE;
+      a.cu_seqlens = pro->cu_seqlens;
+    }
     if (pro->raw_gates && (!pro->A_log || !pro->dt_bias || !aligned_elem(pro->A_log, GDN_F32) ||
                            !aligned_elem(pro->dt_bias, GDN_F32)))
       return GDN_ERROR_INVALID_VALUE;
@@ -90,7 +97,9 @@ gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, con
   const size_t state_bytes = (size_t)BH * (size_t)(a.D * a.D) * sizeof(float);
   const size_t in_elem = a.in_dtype == GDN_F32 ? 4 : 2;
   const size_t out_elem = a.out_dtype == GDN_F32 ? 4 : 2;
-  const size_t o_bytes = (size_t)BH * (size_t)a.T * (size_t)a.D * out_elem;
+  // a ragged batch packs all sequences into H * T rows (T = total tokens)
+  const size_t o_rows = a.cu_seqlens ? (size_t)a.H * (size_t)a.T : (size_t)BH * (size_t)a.T;
+  const size_t o_bytes = o_rows * (size_t)a.D * out_elem;
   if (a.T > 0) {
     if (!q || !k || !v || !beta || !log_alpha || !o) return GDN_ERROR_INVALID_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GDN_ERROR_INVALID_VALUE;
@@ -159,10 +168,10 @@ gdn_status_t kda_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void*
 
 gdn_status_t gdn_chunk_fwd_ex(const gdn_chunk_ex_desc_t* d, const void* q, const void* k, const void* v,
                               const void* beta, const void* log_alpha, const float* A_log,
-                              const float* dt_bias, const float* s0, void* o, float* s_final,
-                              float* s_ckpt, void* stream) {
+                              const float* dt_bias, const int32_t* cu_seqlens, const float* s0, void* o,
+                              float* s_final, float* s_ckpt, void* stream) {
   if (!d || d->reserved != 0) return GDN_ERROR_INVALID_VALUE;
-  const Prologue pro = {d->H_qk, d->raw_gates, A_log, dt_bias};
+  const Prologue pro = {d->H_qk, d->raw_gates, A_log, dt_bias, cu_seqlens};
   return chunk_fwd(0, &d->base, q, k, v, beta, log_alpha, s0, o, s_final, s_ckpt, nullptr, 0, stream, &pro);
 }
 

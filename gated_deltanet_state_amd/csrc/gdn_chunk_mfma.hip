@@ -210,6 +210,14 @@ __device__ __forceinline__ h4 col_tr(const _Float16* base, int ld, int r0, int c
   return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)(a)));
 }
 
+// Where one (sequence, value head) stream lives: its token count, the element offset of its
+// rows in q and k, the token offset of its rows in v, o and of its gates, and the index of its
+// states in s0, s_final and s_ckpt.  A batch of equal-length sequences is [B, H(qk), T, D]; a
+// ragged batch concatenates the sequences, each in that layout with its own length.
+struct Stream {
+  int64_t T, qk, tok, st;
+};
+
 // ------------------------------------------------------------------------------------------
 // Role: state chain (waves 0, 1).  The wave owns value rows dv = c0 + 16 db + (0..15) and all
 // 128 key channels: St[kb] is the accumulator tile (d_k block kb, d_v block db) of S^T, lane
@@ -219,10 +227,10 @@ __device__ __forceinline__ h4 col_tr(const _Float16* base, int ld, int r0, int c
 // S^T <- gamma_63 S^T + (diag(e^{G_63 - G}) K)^T U.  Its A operand, the decayed transposed keys,
 // is staged by the output waves in two halves: tokens 0..31 one phase ahead (fetched with the
 // other phase-1 operands) and tokens 32..63 in phase 1 (fetched at the start of phase 2).
-__device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, int64_t bh, int c0, int db, int l,
+__device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, const Stream& str, int c0, int db, int l,
                                            int64_t nchunks) {
   const int lr = l & 15, lg = l >> 4, dv = 16 * db + lr, sg = swl(l);
-  const int64_t T = p.T;
+  const int64_t T = str.T, bh = str.st;
   f4 St[8];
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) {
@@ -345,8 +353,8 @@ struct RowStage {
   __amdgpu_buffer_rsrc_t r;
   v4u x[8];
   int ch, rq;
-  __device__ __forceinline__ RowStage(const void* base, const ChunkArgs& p, int64_t bh, int l)
-      : r(stream_rsrc(base, bh * p.T * D, p.T * D)), ch(l & 15), rq(l >> 4) {}
+  __device__ __forceinline__ RowStage(const void* base, const Stream& str, int l)
+      : r(stream_rsrc(base, str.qk, str.T * D)), ch(l & 15), rq(l >> 4) {}
   __device__ __forceinline__ void load(int64_t t0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = ld_b128(r, (t0 + 32 * half + 4 * i + rq) * D + 8 * ch);
@@ -378,9 +386,10 @@ __device__ __forceinline__ void stage_kt(Smem& sm, const _Float16* k, const Gate
 // d_k blocks 2 tb0 .. 2 tb0 + 3: tokens 32..63 of chunk c in phase 1 and tokens 0..31 of chunk
 // c + 1 in phase 2 (each half is read by the chain in the phase after it is written).
 template <typename TOut, int tb0>
-__device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, int64_t bh, int c0, int l, int64_t nchunks) {
+__device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, const Stream& str, int c0, int l,
+                                         int64_t nchunks) {
   const int lr = l & 15, lg = l >> 4, sg = swl(l);
-  const int64_t T = p.T, tok0 = bh * T;
+  const int64_t T = str.T, tok0 = str.tok;
   const auto orr = __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<TOut*>(p.o) + tok0 * D), 0,
                                                      (int)(T * D * (int64_t)sizeof(TOut)), kRsrcWord3);
   __syncthreads();
@@ -536,9 +545,10 @@ __device__ __forceinline__ void toff_part(Smem& sm, int64_t c, int l) {
 // previous phase 2), and part COLS = half of the off-diagonal blocks of T for chunk c + 1
 // (phase 2).
 template <int half>
-__device__ __forceinline__ void key_toff_role(Smem& sm, const ChunkArgs& p, int64_t bhq, int l, int64_t nchunks) {
+__device__ __forceinline__ void key_toff_role(Smem& sm, const ChunkArgs& p, const Stream& str, int l,
+                                              int64_t nchunks) {
   // two register sets: each chunk's rows are loaded two iterations before they are stored
-  RowStage<half> ka(p.k, p, bhq, l), kb(p.k, p, bhq, l);
+  RowStage<half> ka(p.k, str, l), kb(p.k, str, l);
   ka.load(0);
   kb.load(C);
   auto iter = [&](int c, RowStage<half>& ks) {
@@ -559,12 +569,12 @@ __device__ __forceinline__ void key_toff_role(Smem& sm, const ChunkArgs& p, int6
 // second half of the queries and the value slice of chunk c + 1 (phase 2; every reader of those
 // buffers runs in phase 1).
 template <bool RAW>
-__device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int64_t bh, int64_t bhq, int c0, int l,
+__device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, const Stream& str, int c0, int l,
                                               int64_t nchunks) {
-  const int64_t tok0 = bh * p.T;
-  const auto br = stream_rsrc(p.beta, tok0, p.T);
-  const auto gr = stream_rsrc(p.log_alpha, tok0, p.T);
-  const auto vr = stream_rsrc(p.v, tok0 * D, p.T * D);
+  const int64_t tok0 = str.tok, T = str.T;
+  const auto br = stream_rsrc(p.beta, tok0, T);
+  const auto gr = stream_rsrc(p.log_alpha, tok0, T);
+  const auto vr = stream_rsrc(p.v, tok0 * D, T * D);
   // values: channels c0 + 8 dq .., tokens 4 vq .. 4 vq + 3; with the 16 token groups on
   // consecutive lanes the transposed 8-byte stores are free of LDS bank conflicts
   const int dq = l >> 4, vq = l & 15;
@@ -572,7 +582,7 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int6
     uint32_t bb, gg;
     v4u vv[4];
   };
-  RowStage<1> qa(p.q, p, bhq, l), qb(p.q, p, bhq, l);
+  RowStage<1> qa(p.q, str, l), qb(p.q, str, l);
   Set sa, sb;
   auto load_g = [&](Set& st, int64_t t0) {
     st.bb = __builtin_amdgcn_raw_buffer_load_b16(br, (int)((t0 + l) * 2), 0, 0);
@@ -593,7 +603,7 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int6
   // raw gate projections (layer prologue): beta = sigmoid(b), log alpha = -exp(A_log) softplus(a + dt_bias)
   float Aexp = 0.f, dtb = 0.f;
   if constexpr (RAW) {
-    const int64_t h = bh % p.H;
+    const int64_t h = str.st % p.H;
     Aexp = __expf(p.A_log[h]);
     dtb = p.dt_bias[h];
   }
@@ -602,7 +612,7 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int6
       float g = bf16_bits_to_f32(st.gg & 0xffffu), bt = bf16_bits_to_f32(st.bb & 0xffffu);
       if constexpr (RAW) {
         // tokens past the end read as b = a = 0; they must stay identity steps
-        const bool live = (int64_t)(c + 2) * C + l < p.T;
+        const bool live = (int64_t)(c + 2) * C + l < T;
         const float xa = g + dtb;
         g = live ? -Aexp * (fmaxf(xa, 0.f) + log1pf(__expf(-fabsf(xa)))) : 0.f;
         bt = live ? 1.f / (1.f + __expf(-bt)) : 0.f;
@@ -649,8 +659,8 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, int6
 }
 
 // Role: first half of the queries of chunk c + 1 (wave 9, phase 2), loaded two iterations ahead.
-__device__ __forceinline__ void q_role(Smem& sm, const ChunkArgs& p, int64_t bhq, int l, int64_t nchunks) {
-  RowStage<0> qa(p.q, p, bhq, l), qb(p.q, p, bhq, l);
+__device__ __forceinline__ void q_role(Smem& sm, const ChunkArgs& p, const Stream& str, int l, int64_t nchunks) {
+  RowStage<0> qa(p.q, str, l), qb(p.q, str, l);
   qa.load(-C);
   qb.load(0);
   auto iter = [&](int c, RowStage<0>& qs) {
@@ -760,9 +770,22 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
   if (nblk % (8 * NT) == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
   const int c0 = (int)(bid % NT) * DVT;
   const int64_t bh = bid / NT;
-  // value head h of batch b reads query/key head h / (H / Hqk)
-  const int64_t bhq = (bh / p.H) * p.Hqk + (bh % p.H) / (p.H / p.Hqk);
-  const int64_t nchunks = (p.T + C - 1) / C;
+  // value head h of sequence b reads query/key head h / (H / Hqk)
+  const int64_t b = bh / p.H, h = bh % p.H, hq = h / (p.H / p.Hqk);
+  Stream str;
+  str.st = bh;
+  if (p.cu_seqlens) {  // offsets clamped into [0, T]: any table keeps every access inside the tensors
+    const int64_t t0 = min(max((int64_t)p.cu_seqlens[b], (int64_t)0), p.T);
+    const int64_t t1 = min(max((int64_t)p.cu_seqlens[b + 1], t0), p.T);
+    str.T = t1 - t0;
+    str.qk = (p.Hqk * t0 + hq * str.T) * D;
+    str.tok = p.H * t0 + h * str.T;
+  } else {
+    str.T = p.T;
+    str.qk = (b * p.Hqk + hq) * p.T * D;
+    str.tok = bh * p.T;
+  }
+  const int64_t nchunks = (str.T + C - 1) / C;
 
   // T and P start at zero; their upper blocks are never written
   for (int e = tid; e < 2 * C * LC / 8; e += NTH) reinterpret_cast<v4u*>(&sm.t[0][0][0])[e] = v4u{0u, 0u, 0u, 0u};
@@ -775,16 +798,16 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
     case 0:
     case 1:
       __builtin_amdgcn_s_setprio(2);
-      chain_role(sm, p, bh, c0, w, l, nchunks);
+      chain_role(sm, p, str, c0, w, l, nchunks);
       break;
     case 2: tdiag_role<0>(sm, l, nchunks); break;
     case 3: tdiag_role<2>(sm, l, nchunks); break;
-    case 4: out_role<TOut, 0>(sm, p, bh, c0, l, nchunks); break;
-    case 5: out_role<TOut, 2>(sm, p, bh, c0, l, nchunks); break;
-    case 6: key_toff_role<0>(sm, p, bhq, l, nchunks); break;
-    case 7: key_toff_role<1>(sm, p, bhq, l, nchunks); break;
-    case 8: gates_qv_role<RAW>(sm, p, bh, bhq, c0, l, nchunks); break;
-    case 9: q_role(sm, p, bhq, l, nchunks); break;
+    case 4: out_role<TOut, 0>(sm, p, str, c0, l, nchunks); break;
+    case 5: out_role<TOut, 2>(sm, p, str, c0, l, nchunks); break;
+    case 6: key_toff_role<0>(sm, p, str, l, nchunks); break;
+    case 7: key_toff_role<1>(sm, p, str, l, nchunks); break;
+    case 8: gates_qv_role<RAW>(sm, p, str, c0, l, nchunks); break;
+    case 9: q_role(sm, p, str, l, nchunks); break;
     case 10: pa_role<0>(sm, l, nchunks); break;
     default: pa_role<1>(sm, l, nchunks); break;
   }

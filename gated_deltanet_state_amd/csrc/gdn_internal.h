@@ -25,6 +25,7 @@ struct ChunkArgs {
   int64_t Hqk;             // query/key heads (H a multiple); equals H for the plain entry points
   int raw_gates;           // beta / log_alpha carry the raw b / a projections
   const float *A_log, *dt_bias;  // [H], raw gates only
+  const int32_t* cu_seqlens;     // [B + 1] token offsets of a ragged batch (T = total), or null
 };
 
 struct DecodeArgs {

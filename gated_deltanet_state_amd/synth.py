@@ -203,3 +203,9 @@ def make_prefill_ex(B: int, H: int, Hqk: int, T: int, D: int, dtype: torch.dtype
     s0 = (torch.randn(B, H, D, D, generator=g) * s0_std) if s0_std > 0 else None
     return {"q": q.to(dtype), "k": k.to(dtype), "v": v.to(dtype), "beta": beta.to(dtype),
             "log_alpha": log_alpha.to(dtype), "s0": s0, "A_log": A_log, "dt_bias": dt_bias}
+
+
+def ragged_lengths(B: int, lo: int, hi: int, seed: int = 0):
+    """Seeded prompt lengths, uniform in [lo, hi] (ragged tails included)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    return [int(x) for x in torch.randint(lo, hi + 1, (B,), generator=g)]

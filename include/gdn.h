@@ -131,14 +131,22 @@ gdn_status_t kda_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void*
  *    a multiple of H_qk); value head h reads query/key head h / (base.H / H_qk);
  *  - raw_gates = 1: beta and log_alpha carry the layer's raw projections b and a, and the
  *    kernel forms beta = sigmoid(b), log alpha = -exp(A_log) softplus(a + dt_bias)
- *    ("Attention, Part 4", section "Where alpha and beta come from").
+ *    ("Attention, Part 4", section "Where alpha and beta come from");
+ *  - a ragged batch (cu_seqlens != NULL): B sequences of different lengths prefilled in one
+ *    call, as a serving engine admits new prompts.  Sequence b holds tokens
+ *    cu_seqlens[b] .. cu_seqlens[b+1] - 1 of T = cu_seqlens[B] in all; every per-token
+ *    tensor is the concatenation of the sequences, each in the layout below with its own
+ *    length (q of sequence b is [H_qk, T_b, Dk], starting at row H_qk * cu_seqlens[b]).
  *
- *   q, k      [B, H_qk, T, Dk]   in_dtype
- *   v         [B, H, T, Dv]; beta, log_alpha [B, H, T]; s0, o, s_final, s_ckpt as in
- *             gdn_chunk_fwd
+ *   q, k      [B, H_qk, T, Dk]   in_dtype (ragged: H_qk * T rows of Dk, as above)
+ *   v         [B, H, T, Dv]; beta, log_alpha [B, H, T] (ragged: H * T rows); s0, o,
+ *             s_final, s_ckpt as in gdn_chunk_fwd (o ragged like v)
  *   A_log, dt_bias [H] fp32, required when raw_gates = 1, ignored otherwise
+ *   cu_seqlens [B + 1] int32 device array, non-decreasing from 0 to T, or NULL.  Values out
+ *             of that order are clamped into [0, T] (a sequence can come out empty), never
+ *             used to address outside the tensors.  Snapshots need ckpt_every = 0 here.
  * Supported on the matrix-core path (bf16 inputs, Dk = Dv = 128, chunk = 64); with
- * H_qk = H and raw_gates = 0 every combination gdn_chunk_fwd supports.  q and k are used
+ * H_qk = H, raw_gates = 0 and no cu_seqlens every combination gdn_chunk_fwd supports.  q and k are used
  * as given: normalise them before the call.  `reserved` must be 0.
  */
 typedef struct {
@@ -150,8 +158,8 @@ typedef struct {
 
 gdn_status_t gdn_chunk_fwd_ex(const gdn_chunk_ex_desc_t* d, const void* q, const void* k, const void* v,
                               const void* beta, const void* log_alpha, const float* A_log,
-                              const float* dt_bias, const float* s0, void* o, float* s_final,
-                              float* s_ckpt, void* stream);
+                              const float* dt_bias, const int32_t* cu_seqlens, const float* s0, void* o,
+                              float* s_final, float* s_ckpt, void* stream);
 
 /*
  * One recurrent (decode) step of the gated delta rule for every live sequence: each

@@ -158,3 +158,27 @@ def forward_ex(q, k, v, beta, log_alpha, s0=None, *, raw_gates: bool = False, A_
         beta, log_alpha = widen(beta), widen(log_alpha)
     s0 = None if s0 is None else widen(s0)
     return forward(q, k, v, beta, log_alpha, s0, ckpt_every=ckpt_every)
+
+
+def forward_ragged(q, k, v, beta, log_alpha, cu_seqlens, *, H: int, Hqk: int, s0=None, raw_gates: bool = False,
+                   A_log=None, dt_bias=None):
+    """A ragged batch: sequence b is tokens cu[b] .. cu[b+1]-1, each per-token tensor being the
+    concatenation of the sequences in their own [heads, T_b, ...] layout (q, k [Hqk * T, D];
+    v [H * T, D]; beta, log_alpha [H * T]; s0 [B, H, D, D] or None).  Each sequence runs
+    through ``forward_ex`` on its own.  Returns (o [H * T, D], s_final [B, H, D, D])."""
+    cu = widen_int(cu_seqlens)
+    q, k, v, beta, log_alpha = widen(q), widen(k), widen(v), widen(beta), widen(log_alpha)
+    B, D = len(cu) - 1, q.shape[1]
+    s0 = None if s0 is None else widen(s0)
+    o = np.empty((v.shape[0], D))
+    sf = np.empty((B, H, D, D))
+    for b in range(B):
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        n = t1 - t0
+        sl = lambda x, h: x[h * t0:h * t1].reshape(h, n, *x.shape[1:])[None]
+        ob, sfb, _ = forward_ex(sl(q, Hqk), sl(k, Hqk), sl(v, H), sl(beta, H), sl(log_alpha, H),
+                                None if s0 is None else s0[b:b + 1], raw_gates=raw_gates, A_log=A_log,
+                                dt_bias=dt_bias)
+        o[H * t0:H * t1] = ob[0].reshape(H * n, D)
+        sf[b] = sfb[0]
+    return o, sf

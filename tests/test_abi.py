@@ -168,7 +168,8 @@ def test_decode_ex_validation_errors(g):
 def test_chunk_ex_validation_errors(g):
     INV, NS, OK = g.GDN_ERROR_INVALID_VALUE, g.GDN_ERROR_NOT_SUPPORTED, g.GDN_SUCCESS
     f = g.lib.gdn_chunk_fwd_ex
-    p = [ctypes.c_void_p(FAKE + i * 0x1000000) for i in range(11)]
+    p = [ctypes.c_void_p(FAKE + i * 0x1000000) for i in range(12)]
+    p[7] = None  # cu_seqlens: not ragged unless a test sets it
 
     def call(d, **kw):
         q = list(p)
@@ -185,6 +186,8 @@ def test_chunk_ex_validation_errors(g):
     assert call(ex(h_qk=0)) == INV
     assert call(ex(raw=2)) == INV
     assert call(ex(raw=1), a5=None) == INV                # A_log missing
+    assert call(ex(ckpt_every=64), a7=ctypes.c_void_p(FAKE + 0x7000000)) == NS   # ragged + snapshots
+    assert call(ex(), a7=ctypes.c_void_p(FAKE + 0x7000002)) == INV              # misaligned cu_seqlens
     assert call(ex(in_dtype=g.GDN_F32)) == NS             # grouped heads: matrix-core path only
     assert call(ex(h_qk=4, in_dtype=g.GDN_F32, Dk=16, Dv=16, chunk=16)) != NS   # plain: vector path
     assert call(ex(B=0)) == OK

@@ -67,3 +67,60 @@ def test_chunk_ex_grouped_32_16_heads():
                                           raw_gates=True, A_log=inp["A_log"], dt_bias=inp["dt_bias"])
     assert rel_l2(o, o_ref) <= 1e-3
     assert rel_l2(sf, sf_ref) <= 2e-3
+
+
+@pytest.mark.parametrize("raw", [False, True])
+def test_ragged_batch(raw):
+    """Six sequences of lengths 130, 64, 1, 0, 200, 65 (ragged tails, a single token, an empty
+    one) prefilled in one call; per-sequence outputs and final states against the oracle."""
+    import gated_deltanet_state_amd as g
+    lens = [130, 64, 1, 0, 200, 65]
+    B, H, Hqk, D = len(lens), 4, 2, 128
+    say(f"ragged batch raw={raw}")
+    seqs = [synth.make_prefill_ex(1, H, Hqk, n, D, raw=raw, seed=100 + i) for i, n in enumerate(lens)]
+    cat = lambda key, heads: torch.cat([s_[key][0].reshape(heads * s_[key].shape[2], *s_[key].shape[3:])
+                                        for s_ in seqs], 0)
+    q, k, v = cat("q", Hqk), cat("k", Hqk), cat("v", H)
+    beta, la = cat("beta", H), cat("log_alpha", H)
+    s0 = torch.cat([s_["s0"] for s_ in seqs], 0)
+    A_log, dt = seqs[0]["A_log"], seqs[0]["dt_bias"]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    o, sf = g.gdn_chunk_fwd_ragged(q.cuda(), k.cuda(), v.cuda(), beta.cuda(), la.cuda(), cu.cuda(), H=H, H_qk=Hqk,
+                                   s0=s0.cuda(), A_log=None if A_log is None else A_log.cuda(),
+                                   dt_bias=None if dt is None else dt.cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, sf_ref = serving.forward_ragged(q, k, v, beta, la, cu, H=H, Hqk=Hqk, s0=s0, raw_gates=raw,
+                                           A_log=A_log, dt_bias=dt)
+    assert rel_l2(o, o_ref) <= 1e-3
+    assert rel_l2(sf, sf_ref) <= 2e-3
+    assert torch.equal(sf[3].cpu(), s0[3])   # the empty sequence keeps its state exactly
+
+
+def test_ragged_equal_lengths_bitwise():
+    """Equal lengths: the ragged call is the batched call, bit for bit."""
+    import gated_deltanet_state_amd as g
+    B, H, T, D = 3, 4, 192, 128
+    inp = synth.make_prefill(B, H, T, D, D, seed=12)
+    d = {k: v.cuda() for k, v in inp.items()}
+    a = g.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["s0"])
+    cu = torch.tensor([0, T, 2 * T, 3 * T], dtype=torch.int32, device="cuda")
+    o, sf = g.gdn_chunk_fwd_ragged(d["q"].reshape(-1, D), d["k"].reshape(-1, D), d["v"].reshape(-1, D),
+                                   d["beta"].reshape(-1), d["log_alpha"].reshape(-1), cu, H=H, s0=d["s0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o.reshape(B, H, T, D), a[0]) and torch.equal(sf, a[1])
+
+
+def test_ragged_bad_offsets_stay_in_bounds():
+    """Offsets out of order are clamped: the call completes and the clamped sequences come out
+    empty (state unchanged)."""
+    import gated_deltanet_state_amd as g
+    H, D, T = 2, 128, 128
+    inp = synth.make_prefill(1, H, T, D, D, seed=13)
+    d = {k: v.cuda() for k, v in inp.items()}
+    s0 = torch.randn(3, H, D, D, device="cuda") * 0.01
+    cu = torch.tensor([0, 100, 40, 10**6], dtype=torch.int32, device="cuda")   # 100 > 40, end past T
+    o, sf = g.gdn_chunk_fwd_ragged(d["q"].reshape(-1, D), d["k"].reshape(-1, D), d["v"].reshape(-1, D),
+                                   d["beta"].reshape(-1), d["log_alpha"].reshape(-1), cu, H=H, s0=s0)
+    torch.cuda.synchronize()
+    assert torch.equal(sf[1], s0[1])           # [100, 40) clamps to empty
+    assert torch.isfinite(o).all() and torch.isfinite(sf).all()

@@ -181,3 +181,26 @@ def test_forward_ex_matches_decode_windows():
                                b.transpose(0, 2, 1), a.transpose(0, 2, 1), raw_gates=True, A_log=A_log, dt_bias=dt)
     assert np.allclose(o, ow.transpose(0, 2, 1, 3), rtol=0, atol=1e-13)
     assert np.allclose(sf, pool, rtol=0, atol=1e-13)
+
+
+def test_ragged_equal_lengths_is_the_batch():
+    """With equal lengths the concatenated layout is the batched [B, H, T, D] one: the ragged
+    oracle and forward_ex agree exactly; an empty sequence keeps its state."""
+    rng = np.random.default_rng(8)
+    B, H, Hqk, T, D = 3, 4, 2, 6, 8
+    q = rng.normal(0, 1, (B, Hqk, T, D))
+    k = rng.normal(0, 1, (B, Hqk, T, D))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.normal(0, 1, (B, H, T, D))
+    beta, la = rng.uniform(0.1, 0.9, (B, H, T)), rng.uniform(-0.2, -0.01, (B, H, T))
+    s0 = rng.normal(0, 0.1, (B, H, D, D))
+    o, sf, _ = serving.forward_ex(q, k, v, beta, la, s0)
+    cu = [0, T, 2 * T, 3 * T]
+    orag, sfrag = serving.forward_ragged(q.reshape(-1, D), k.reshape(-1, D), v.reshape(-1, D), beta.reshape(-1),
+                                         la.reshape(-1), cu, H=H, Hqk=Hqk, s0=s0)
+    assert np.array_equal(orag, o.reshape(-1, D)) and np.array_equal(sfrag, sf)
+    # lengths 6, 0, 12: the empty sequence leaves s0 untouched
+    cu2 = [0, T, T, 3 * T]
+    _, sf2 = serving.forward_ragged(q.reshape(-1, D), k.reshape(-1, D), v.reshape(-1, D), beta.reshape(-1),
+                                    la.reshape(-1), cu2, H=H, Hqk=Hqk, s0=s0)
+    assert np.array_equal(sf2[1], s0[1]) and np.array_equal(sf2[0], sf[0])
