@@ -75,7 +75,7 @@ def test_window_verify_then_commit(D, dtype, kda, raw):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_window_equals_single_steps(dtype):
     """T = 1 windows through the slot table, repeated, equal one commit of the whole window
-    on the GPU, and the plain decode step on identity slots."""
+    on the GPU bit for bit, and match the plain decode step."""
     import gated_deltanet_state_amd as g
     N, T, H, D = 5, 4, 3, 128
     say(f"decode_ex single steps dtype={dtype}")
@@ -138,3 +138,24 @@ def test_verify_workload_full_size_sampled():
     assert rel_l2(d["pool"][torch.as_tensor(rows)], pool_ref) <= 2e-3
     unused = np.setdiff1d(np.arange(c.P), inp["slots"].numpy())
     assert torch.equal(d["pool"][torch.as_tensor(unused)], pool0[torch.as_tensor(unused)])
+
+
+@pytest.mark.parametrize("T", [2, 4, 5, 8])
+@pytest.mark.parametrize("kda,raw", [(False, False), (True, False), (False, True)])
+def test_window_lengths_d128(T, kda, raw):
+    """Windows of 2, 4, 5 and 8 tokens at d = 128, plain, KDA and with the fused prologue."""
+    import gated_deltanet_state_amd as g
+    N, H, Hqk, D, P = 6, 4, 2, 128, 9
+    say(f"decode_ex d128 T={T} kda={kda} raw={raw}")
+    inp = synth.make_serving(N, T, H, Hqk, D, P, torch.float32, kda=kda, raw=raw, seed=40 + T + 3 * kda + 7 * raw,
+                             skip_every=4)
+    d = _cuda(inp)
+    kw = dict(slots=d["slots"], kda=kda, qk_l2norm=raw, A_log=d["A_log"], dt_bias=d["dt_bias"])
+    o = g.gdn_decode_verify(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], **kw)
+    g.gdn_decode_commit(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["n_commit"], **kw)
+    torch.cuda.synchronize()
+    o_ref, _ = _ref(inp, kda=kda, raw=raw, write_state=False)
+    _, pool_ref = _ref(inp, kda=kda, raw=raw, write_state=True)
+    live = _live(inp)
+    assert rel_l2(o[torch.as_tensor(live)], o_ref[live]) <= 1e-5
+    assert rel_l2(d["pool"], pool_ref) <= 1e-5
