@@ -9,8 +9,10 @@ Everything here is a plain composition of pinned pieces:
   * ``gates_from_raw``   -- beta and log alpha from the raw per-head projections.
                             Pinned by closed forms (sigmoid(0) = 1/2, softplus(0) = ln 2,
                             softplus(ln(e - 1)) = 1, limits, sign of log alpha).
-  * ``forward_ex``       -- the prefill with grouped query/key heads and raw gates: the
-                            pinned ``oracle.forward`` on repeated heads and gates_from_raw.
+  * ``forward_ex``       -- the prefill with grouped query/key heads, raw gates and the q/k
+                            normalisation: the pinned ``oracle.forward`` on repeated heads,
+                            gates_from_raw and l2_normalize.  Pinned also by invariance of
+                            the normalised form to a positive scale of each q, k row.
   * ``decode_window``    -- T tokens per sequence on slot-addressed states, each token one
                             call of the pinned single-token step (``oracle.decode_step``).
                             Pinned against the independent token loop of ``oracle.forward``
@@ -136,14 +138,17 @@ def widen_int(x) -> np.ndarray:
 
 
 def forward_ex(q, k, v, beta, log_alpha, s0=None, *, raw_gates: bool = False, A_log=None, dt_bias=None,
-               ckpt_every: int = 0):
+               ckpt_every: int = 0, qk_l2norm: bool = False):
     """The token-loop forward pass (``oracle.forward``) with H value heads reading
-    Hqk = q.shape[1] query/key heads (value head h reads head h // (H / Hqk)), and with the
+    Hqk = q.shape[1] query/key heads (value head h reads head h // (H / Hqk)), with the
     raw gate projections b, a turned into beta and log alpha by ``gates_from_raw`` when
-    ``raw_gates``.  q, k [B, Hqk, T, Dk]; v [B, H, T, Dv]; beta, log_alpha [B, H, T] (b, a for
+    ``raw_gates``, and with every q and k row scaled to unit length by ``l2_normalize`` when
+    ``qk_l2norm``.  q, k [B, Hqk, T, Dk]; v [B, H, T, Dv]; beta, log_alpha [B, H, T] (b, a for
     raw gates; A_log, dt_bias [H]).  Returns (o, s_final, s_ckpt) in fp64."""
     from . import forward
     q, k, v = widen(q), widen(k), widen(v)
+    if qk_l2norm:
+        q, k = l2_normalize(q), l2_normalize(k)
     B, Hqk, T, Dk = q.shape
     H = v.shape[1]
     if H % Hqk != 0:
@@ -161,7 +166,7 @@ def forward_ex(q, k, v, beta, log_alpha, s0=None, *, raw_gates: bool = False, A_
 
 
 def forward_ragged(q, k, v, beta, log_alpha, cu_seqlens, *, H: int, Hqk: int, s0=None, raw_gates: bool = False,
-                   A_log=None, dt_bias=None):
+                   A_log=None, dt_bias=None, qk_l2norm: bool = False):
     """A ragged batch: sequence b is tokens cu[b] .. cu[b+1]-1, each per-token tensor being the
     concatenation of the sequences in their own [heads, T_b, ...] layout (q, k [Hqk * T, D];
     v [H * T, D]; beta, log_alpha [H * T]; s0 [B, H, D, D] or None).  Each sequence runs
@@ -178,7 +183,7 @@ def forward_ragged(q, k, v, beta, log_alpha, cu_seqlens, *, H: int, Hqk: int, s0
         sl = lambda x, h: x[h * t0:h * t1].reshape(h, n, *x.shape[1:])[None]
         ob, sfb, _ = forward_ex(sl(q, Hqk), sl(k, Hqk), sl(v, H), sl(beta, H), sl(log_alpha, H),
                                 None if s0 is None else s0[b:b + 1], raw_gates=raw_gates, A_log=A_log,
-                                dt_bias=dt_bias)
+                                dt_bias=dt_bias, qk_l2norm=qk_l2norm)
         o[H * t0:H * t1] = ob[0].reshape(H * n, D)
         sf[b] = sfb[0]
     return o, sf

@@ -204,3 +204,43 @@ def test_ragged_equal_lengths_is_the_batch():
     _, sf2 = serving.forward_ragged(q.reshape(-1, D), k.reshape(-1, D), v.reshape(-1, D), beta.reshape(-1),
                                     la.reshape(-1), cu2, H=H, Hqk=Hqk, s0=s0)
     assert np.array_equal(sf2[1], s0[1]) and np.array_equal(sf2[0], sf[0])
+
+
+def test_forward_ex_l2norm_scale_invariant():
+    """With the q/k normalisation the prefill depends on each q and k row only through its
+    direction: a positive scale per (head, token) row leaves it unchanged (up to the 1e-6
+    epsilon under the square root, negligible at these norms), while without it the result
+    moves.  A missing normalisation, one over the wrong axis, or one applied to q only or k
+    only fails this."""
+    rng = np.random.default_rng(11)
+    B, Hqk, H, T, D = 2, 2, 4, 7, 8
+    q = rng.normal(0, 10, (B, Hqk, T, D))
+    k = rng.normal(0, 10, (B, Hqk, T, D))
+    v = rng.normal(0, 1, (B, H, T, D))
+    beta, la = rng.uniform(0.1, 0.9, (B, H, T)), rng.uniform(-0.2, -0.01, (B, H, T))
+    s0 = rng.normal(0, 0.1, (B, H, D, D))
+    cq = rng.uniform(1, 10, (B, Hqk, T, 1))
+    ck = rng.uniform(1, 10, (B, Hqk, T, 1))
+    o1, sf1, _ = serving.forward_ex(q, k, v, beta, la, s0, qk_l2norm=True)
+    o2, sf2, _ = serving.forward_ex(q * cq, k * ck, v, beta, la, s0, qk_l2norm=True)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-8) and np.allclose(sf1, sf2, rtol=0, atol=1e-8)
+    o3, _, _ = serving.forward_ex(q * cq, k, v, beta, la, s0, qk_l2norm=False)
+    o4, _, _ = serving.forward_ex(q, k, v, beta, la, s0, qk_l2norm=False)
+    assert not np.allclose(o3, o4, rtol=0, atol=1e-3)
+
+
+def test_forward_ex_l2norm_keeps_unit_rows():
+    """Rows that already have unit length are scaled by 1 / sqrt(1 + 1e-6) only: the
+    normalised prefill matches the plain one to that factor."""
+    rng = np.random.default_rng(12)
+    B, H, T, D = 1, 2, 9, 8
+    q = rng.normal(0, 1, (B, H, T, D))
+    k = rng.normal(0, 1, (B, H, T, D))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.normal(0, 1, (B, H, T, D))
+    beta, la = rng.uniform(0.1, 0.9, (B, H, T)), rng.uniform(-0.2, -0.01, (B, H, T))
+    o1, sf1, _ = serving.forward_ex(q, k, v, beta, la, qk_l2norm=True)
+    o2, sf2, _ = serving.forward_ex(q, k, v, beta, la)
+    assert np.allclose(o1, o2, rtol=1e-5, atol=1e-6) and np.allclose(sf1, sf2, rtol=1e-5, atol=1e-6)
+    assert not np.array_equal(o1, o2)
