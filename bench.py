@@ -278,18 +278,19 @@ def main():
         B, H, Hqk, T, D = 2, 32, 16, 4096, 128
         log("prefill_ex: generating inputs")
         d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
-             for k, v in synth.make_prefill_ex(B, H, Hqk, T, D, raw=True, s0_std=0.01, seed=2003).items()}
+             for k, v in synth.make_prefill_ex(B, H, Hqk, T, D, raw=True, unit=False, s0_std=0.01, seed=2003).items()}
         o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
         sf = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
         ms = time_launches(lambda i: g.gdn_chunk_fwd_ex(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["s0"],
-                                                         A_log=d["A_log"], dt_bias=d["dt_bias"], o=o, s_final=sf),
+                                                         A_log=d["A_log"], dt_bias=d["dt_bias"], qk_l2norm=True,
+                                                         o=o, s_final=sf),
                            20, 3, torch)
         # q, k once per query/key head; v, b, a, o per value head; s0 and s_final
         nb = B * T * (2 * Hqk * D + H * (D + 2)) * 2 + B * H * T * D * 2 + 2 * B * H * D * D * 4
         fl = B * H * T * prefill_flops_per_head_token(64, D)
         gb = nb / (ms * 1e-3) / 1e9
-        extra["prefill_grouped_raw_gates"] = {
-            "workload": "gdn_prefill_grouped32x16_rawgates_bf16", "B": B, "H": H, "H_qk": Hqk, "T": T, "d": D,
+        extra["prefill_layer_prologue"] = {
+            "workload": "gdn_prefill_grouped32x16_rawgates_qknorm_bf16", "B": B, "H": H, "H_qk": Hqk, "T": T, "d": D,
             "us": round(ms * 1e3, 2), "Mtok_per_s": round(B * T / (ms * 1e-3) / 1e6, 3),
             "roofline": {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gb / HBM_PEAK_GBS, 4), "traffic": None,

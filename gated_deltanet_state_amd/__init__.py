@@ -44,7 +44,7 @@ class GdnChunkDesc(ctypes.Structure):
 class GdnChunkExDesc(ctypes.Structure):
     """Mirror of gdn_chunk_ex_desc_t."""
     _fields_ = [("base", GdnChunkDesc), ("H_qk", ctypes.c_int64), ("raw_gates", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("qk_l2norm", ctypes.c_int32)]
 
 
 class GdnDecodeExDesc(ctypes.Structure):
@@ -289,15 +289,15 @@ def gdn_decode_commit(pool, q, k, v, beta, log_alpha, n_commit, **kw):
     return gdn_decode_ex(pool, q, k, v, beta, log_alpha, n_commit=n_commit, write_state=True, **kw)
 
 
-def gdn_chunk_fwd_ex(q, k, v, beta, log_alpha, s0=None, *, A_log=None, dt_bias=None, chunk: int = 64,
-                     ckpt_every: int = 0, out_dtype=None, o=None, s_final=None, s_ckpt=None,
+def gdn_chunk_fwd_ex(q, k, v, beta, log_alpha, s0=None, *, A_log=None, dt_bias=None, qk_l2norm: bool = False,
+                     chunk: int = 64, ckpt_every: int = 0, out_dtype=None, o=None, s_final=None, s_ckpt=None,
                      return_final: bool = True, stream=None):
     """Chunkwise prefill with grouped query/key heads and optionally the raw gate projections
-    (gdn_chunk_fwd_ex in include/gdn.h).
+    and the q/k normalisation (gdn_chunk_fwd_ex in include/gdn.h).
 
     q, k [B,Hqk,T,D]; v [B,H,T,D]; beta, log_alpha [B,H,T] (b and a when A_log, dt_bias [H]
-    fp32 are given); s0 [B,H,D,D] fp32 or None.  Returns (o, s_final, s_ckpt) like
-    gdn_chunk_fwd.
+    fp32 are given); s0 [B,H,D,D] fp32 or None; qk_l2norm scales q and k rows to unit length
+    in the kernel.  Returns (o, s_final, s_ckpt) like gdn_chunk_fwd.
     """
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q must be [B, Hqk, T, D] and v [B, H, T, D]")
@@ -331,7 +331,7 @@ def gdn_chunk_fwd_ex(q, k, v, beta, log_alpha, s0=None, *, A_log=None, dt_bias=N
         _check(s_ckpt, "s_ckpt", (B, H, n_ck, D, D), torch.float32, dev)
     else:
         s_ckpt = None
-    d = GdnChunkExDesc(_desc(B, H, T, D, chunk, in_dt, out_dt, ckpt_every), Hqk, int(raw), 0)
+    d = GdnChunkExDesc(_desc(B, H, T, D, chunk, in_dt, out_dt, ckpt_every), Hqk, int(raw), int(bool(qk_l2norm)))
     st = lib.gdn_chunk_fwd_ex(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
                               _ptr(A_log), _ptr(dt_bias), None, _ptr(s0), _ptr(o), _ptr(s_final), _ptr(s_ckpt),
                               _stream(stream))
@@ -360,8 +360,8 @@ def unpack_ragged(packed, cu, heads: int):
 
 
 def gdn_chunk_fwd_ragged(q, k, v, beta, log_alpha, cu_seqlens, *, H: int, H_qk: int = None, s0=None,
-                         A_log=None, dt_bias=None, out_dtype=None, o=None, s_final=None,
-                         return_final: bool = True, stream=None):
+                         A_log=None, dt_bias=None, qk_l2norm: bool = False, out_dtype=None, o=None,
+                         s_final=None, return_final: bool = True, stream=None):
     """Prefill of a ragged batch (gdn_chunk_fwd_ex with cu_seqlens): B sequences of different
     lengths in one call.
 
@@ -397,7 +397,7 @@ def gdn_chunk_fwd_ragged(q, k, v, beta, log_alpha, cu_seqlens, *, H: int, H_qk: 
         s_final = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
     if s_final is not None:
         _check(s_final, "s_final", (B, H, D, D), torch.float32, dev)
-    d = GdnChunkExDesc(_desc(B, H, T, D, 64, in_dt, out_dt, 0), H_qk, int(raw), 0)
+    d = GdnChunkExDesc(_desc(B, H, T, D, 64, in_dt, out_dt, 0), H_qk, int(raw), int(bool(qk_l2norm)))
     st = lib.gdn_chunk_fwd_ex(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
                               _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(s0), _ptr(o), _ptr(s_final),
                               None, _stream(stream))

@@ -60,6 +60,7 @@ gdn_status_t check_chunk_desc(const gdn_chunk_desc_t* d, int is_kda, gdn::ChunkA
 struct Prologue {
   int64_t H_qk;
   int raw_gates;
+  int qk_l2norm;
   const float *A_log, *dt_bias;
   const int32_t* cu_seqlens;  // ragged batch: [B + 1] token offsets, T = total tokens
 };
@@ -74,8 +75,10 @@ gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, con
   if (pro) {
     if (pro->H_qk <= 0 || a.H % pro->H_qk != 0) return GDN_ERROR_INVALID_VALUE;
     if (pro->raw_gates != 0 && pro->raw_gates != 1) return GDN_ERROR_INVALID_VALUE;
+    if (pro->qk_l2norm != 0 && pro->qk_l2norm != 1) return GDN_ERROR_INVALID_VALUE;
     // the prologue runs in the matrix-core kernel only; without one, the plain paths apply
-    if ((pro->H_qk != a.H || pro->raw_gates || pro->cu_seqlens) && !gdn::chunk_mfma_supported(a))
+    if ((pro->H_qk != a.H || pro->raw_gates || pro->qk_l2norm || pro->cu_seqlens) &&
+        !gdn::chunk_mfma_supported(a))
       return GDN_ERROR_NOT_SUPPORTED;
     if (pro->cu_seqlens) {
       if (a.ckpt_every != 0) return GDN_ERROR_NOT_SUPPORTED;  // snapshots need a common length
@@ -87,6 +90,7 @@ gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, con
       return GDN_ERROR_INVALID_VALUE;
     a.Hqk = pro->H_qk;
     a.raw_gates = pro->raw_gates;
+    a.qk_l2norm = pro->qk_l2norm;
     a.A_log = pro->raw_gates ? pro->A_log : nullptr;
     a.dt_bias = pro->raw_gates ? pro->dt_bias : nullptr;
   }
@@ -170,8 +174,8 @@ gdn_status_t gdn_chunk_fwd_ex(const gdn_chunk_ex_desc_t* d, const void* q, const
                               const void* beta, const void* log_alpha, const float* A_log,
                               const float* dt_bias, const int32_t* cu_seqlens, const float* s0, void* o,
                               float* s_final, float* s_ckpt, void* stream) {
-  if (!d || d->reserved != 0) return GDN_ERROR_INVALID_VALUE;
-  const Prologue pro = {d->H_qk, d->raw_gates, A_log, dt_bias, cu_seqlens};
+  if (!d) return GDN_ERROR_INVALID_VALUE;
+  const Prologue pro = {d->H_qk, d->raw_gates, d->qk_l2norm, A_log, dt_bias, cu_seqlens};
   return chunk_fwd(0, &d->base, q, k, v, beta, log_alpha, s0, o, s_final, s_ckpt, nullptr, 0, stream, &pro);
 }
 

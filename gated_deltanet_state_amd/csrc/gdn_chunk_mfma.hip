@@ -33,6 +33,11 @@
 // The products run on v_mfma_f32_16x16x32_f16 / 16x16x16_f16 with fp32 accumulation.
 // bf16 inputs convert exactly to fp16 (|x| <= 65504); derived operands (S, P, U, T) are
 // rounded to fp16, whose 11-bit significand keeps the bf16-output error budget.
+// Layer prologue (optional, template flags): raw gate projections turned into beta and
+// log alpha by the gate-table wave; q/k normalisation as per-token factors 1/|k_r|, 1/|q_r|
+// computed by the staging waves from the exact fp16 rows and applied where the rows are used
+// (Gram tiles, the state chain's beta gamma, the decayed keys, the output rows), so the
+// staged tiles stay exact.
 // Decay factors: inside a 16-token diagonal block e^{G_r - G_j} is formed directly; across
 // blocks it is split at the end of the previous block, e^{G_r - G_ref} * e^{G_ref - G_j},
 // both factors <= 1, so no gate strength can overflow it.
@@ -60,12 +65,13 @@ constexpr int LT = 24;       // row stride (halves) of 16x16 blocks
 struct alignas(16) Gates {
   alignas(16) float G[C];     // inclusive prefix of log alpha
   alignas(16) float gam[C];   // e^{G_r}
-  alignas(16) float dec[C];   // e^{G_63 - G_r}
+  alignas(16) float dec[C];   // e^{G_63 - G_r} / |k_r|
   alignas(16) float beta[C];
   alignas(16) float el[C];    // e^{G_r - G_ref(block of r)}, G_ref(R) = G_{16R-1} (0 for R = 0)
   alignas(16) float nbel[C];  // -beta_r el_r
   alignas(16) float er[3][C]; // er[R-1][j] = e^{G_ref(R) - G_j} for j < 16 R, R = 1..3
-  alignas(16) _Float16 bbg[C][2];  // (beta_r, beta_r gamma_r) in fp16, read by the state chain
+  alignas(16) float rk[C];    // 1 / |k_r| when the kernel normalises the keys
+  alignas(16) _Float16 bbg[C][2];  // (beta_r, beta_r gamma_r / |k_r|) in fp16, read by the state chain
 };
 
 // Buffers hold data of one chunk: keys and gate tables by chunk mod 3, T by chunk mod 2, the
@@ -93,6 +99,7 @@ struct alignas(16) Smem {
   alignas(16) _Float16 an[2][6][16][LT]; // -A, off-diagonal blocks (R, J), R > J, by chunk mod 2
   alignas(16) _Float16 u[DVT][LK];       // U of the chain's chunk                [d_v][token]
   alignas(16) Gates gt[3];
+  alignas(16) float rq[C];               // 1 / |q_r| of the queries' chunk when the kernel normalises them
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
 __device__ __forceinline__ int kbuf(int chunk) { return (chunk + 3) % 3; }  // chunk >= -3
@@ -346,9 +353,37 @@ __device__ __forceinline__ void chain_role(Smem& sm, const ChunkArgs& p, const S
 // issued in the other phase stays in flight across the barriers (buffer loads never touch the
 // LDS counter the barriers wait on).
 
+// Value of x in the partner lane of a DPP row permutation: row_mirror (0x140, lane c of the
+// 16-lane row reads lane 15 - c), row_half_mirror (0x141, 7 - c within each half row),
+// quad_perm 2,3,0,1 (0x4e, c ^ 2) and quad_perm 1,0,3,2 (0xb1, c ^ 1).
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// Reduce-scatter of eight per-lane partial sums ss[i] over the 16 lanes of a DPP row: each
+// exchange pairs lanes from different halves of the set of lanes already summed and keeps half
+// of the rows, so 4 + 2 + 1 + 1 exchanges replace 8 x 4.  Lane c ends with the full sum of row
+// 4 [c >= 8] + 2 [c % 8 >= 4] + [c & 2] (lanes c and c ^ 1 hold the same row); returns it and
+// the row index.
+__device__ __forceinline__ float row16_reduce_scatter(const float (&ss)[8], int c, int& row) {
+  const bool hA = c >= 8, hB = (c & 7) >= 4, hC = (c & 2) != 0;
+  float a[4], b[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = (hA ? ss[j + 4] : ss[j]) + dpp_partner<0x140>(hA ? ss[j] : ss[j + 4]);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) b[m] = (hB ? a[m + 2] : a[m]) + dpp_partner<0x141>(hB ? a[m] : a[m + 2]);
+  const float x = (hC ? b[1] : b[0]) + dpp_partner<0x4e>(hC ? b[0] : b[1]);
+  row = 4 * hA + 2 * hB + hC;
+  return x + dpp_partner<0xb1>(x);
+}
+
 // Half of the row-major tokens of a chunk (rows 32 half + 0..31) of a [token][d_k] bf16 input,
 // converted to fp16 into a chunk-swizzled LDS tile (row 32 half + 4 i + rq has bit 2 = i & 1).
-template <int half>
+// With L2N the tile keeps the rows as given and rn[row] receives 1 / sqrt(sum(x^2) + 1e-6),
+// the factor that scales the row to unit length ("Attention, Part 4", section 6: queries and
+// keys are normalised before the memory step); the consumers apply it per token.  The 16
+// lanes of a row form one DPP row; the squares of the exact fp16 values sum in fp32.
+template <int half, bool L2N>
 struct RowStage {
   __amdgpu_buffer_rsrc_t r;
   v4u x[8];
@@ -359,9 +394,27 @@ struct RowStage {
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = ld_b128(r, (t0 + 32 * half + 4 * i + rq) * D + 8 * ch);
   }
-  __device__ __forceinline__ void store(_Float16 (*dst)[LQ]) const {
+  __device__ __forceinline__ void store(_Float16 (*dst)[LQ], float* rn) const {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    float ss[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<h8*>(&dst[32 * half + 4 * i + rq][8 * (ch ^ (i & 1))]) = bf8_to_h8(x[i]);
+    for (int i = 0; i < 8; ++i) {
+      const h8 y = bf8_to_h8(x[i]);
+      *reinterpret_cast<h8*>(&dst[32 * half + 4 * i + rq][8 * (ch ^ (i & 1))]) = y;
+      if constexpr (L2N) {
+        ss[i] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const h2 pr = {y[2 * e], y[2 * e + 1]};
+          ss[i] = __builtin_amdgcn_fdot2(pr, pr, ss[i], false);
+        }
+      }
+    }
+    if constexpr (L2N) {  // row 4 i + rq of the half: the two lanes holding row i write the same value
+      int i;
+      const float sum = row16_reduce_scatter(ss, ch, i);
+      rn[32 * half + 4 * i + rq] = __builtin_amdgcn_rsqf(sum + 1e-6f);  // argument >= 1e-6: no denormal
+    }
   }
 };
 
@@ -385,7 +438,7 @@ __device__ __forceinline__ void stage_kt(Smem& sm, const _Float16* k, const Gate
 // so rows outside the stream are dropped.  The wave also stages the decayed transposed keys of
 // d_k blocks 2 tb0 .. 2 tb0 + 3: tokens 32..63 of chunk c in phase 1 and tokens 0..31 of chunk
 // c + 1 in phase 2 (each half is read by the chain in the phase after it is written).
-template <typename TOut, int tb0>
+template <typename TOut, int tb0, bool L2N>
 __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, const Stream& str, int c0, int l,
                                          int64_t nchunks) {
   const int lr = l & 15, lg = l >> 4, sg = swl(l);
@@ -418,11 +471,13 @@ __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, const Str
         sched_fence();
       }
     }
+    float rqv[2];  // 1 / |q| of the lane's two output rows (the queries' buffer is refilled in phase 2)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float ga = sm.gt[kbuf(c)].gam[16 * (tb0 + t) + lr];
       Oa[t][0] *= ga;
       Oa[t][1] *= ga;
+      rqv[t] = L2N ? sm.rq[16 * (tb0 + t) + lr] : 1.f;
     }
     stage_kt(sm, &sm.k[kbuf(c)][0][0], sm.gt[kbuf(c)], 2 * tb0, 1, l);
     __syncthreads();
@@ -439,6 +494,7 @@ __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, const Str
       }
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
+        if constexpr (L2N) Oa[t][d] *= rqv[t];  // both terms of the output row carry 1 / |q_r|
         const int off = (int)(((t0 + 16 * tb + lr) * D + c0 + 16 * d + 4 * lg) * (int64_t)sizeof(TOut));
         if constexpr (sizeof(TOut) == 2) {
           typedef unsigned u2v __attribute__((ext_vector_type(2)));
@@ -458,7 +514,7 @@ __device__ __forceinline__ void out_role(Smem& sm, const ChunkArgs& p, const Str
 // diagonal 16x16 blocks of A of chunk c + 2 (decay factors, then the key Gram tiles) and stages
 // them on the diagonal of T's buffer; phase 1 of the next iteration replaces them by their
 // inverses.
-template <int J0>
+template <int J0, bool L2N>
 __device__ __forceinline__ void tdiag_role(Smem& sm, int l, int64_t nchunks) {
   const int lr = l & 15, lg = l >> 4;
   __syncthreads();
@@ -495,6 +551,8 @@ __device__ __forceinline__ void tdiag_role(Smem& sm, int l, int64_t nchunks) {
         }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
+        if constexpr (L2N)  // unit keys: rows and columns of K K^T scale by 1 / |k|
+          dec[j] *= g.rk[16 * (J0 + j) + lr] * *reinterpret_cast<const f4*>(&g.rk[16 * (J0 + j) + 4 * lg]);
         f4 a = dec[j] * acc[j];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -544,15 +602,15 @@ __device__ __forceinline__ void toff_part(Smem& sm, int64_t c, int l) {
 // Role: keys of chunk c + 2, half `half` (waves 6, 7, phase 1; their buffer was last read in the
 // previous phase 2), and part COLS = half of the off-diagonal blocks of T for chunk c + 1
 // (phase 2).
-template <int half>
+template <int half, bool L2N>
 __device__ __forceinline__ void key_toff_role(Smem& sm, const ChunkArgs& p, const Stream& str, int l,
                                               int64_t nchunks) {
   // two register sets: each chunk's rows are loaded two iterations before they are stored
-  RowStage<half> ka(p.k, str, l), kb(p.k, str, l);
+  RowStage<half, L2N> ka(p.k, str, l), kb(p.k, str, l);
   ka.load(0);
   kb.load(C);
-  auto iter = [&](int c, RowStage<half>& ks) {
-    ks.store(sm.k[kbuf(c + 2)]);
+  auto iter = [&](int c, RowStage<half, L2N>& ks) {
+    ks.store(sm.k[kbuf(c + 2)], sm.gt[kbuf(c + 2)].rk);
     ks.load((int64_t)(c + 4) * C);
     __syncthreads();
     toff_part<half>(sm, c, l);
@@ -568,7 +626,7 @@ __device__ __forceinline__ void key_toff_role(Smem& sm, const ChunkArgs& p, cons
 // Role: gate tables of chunk c + 2 (wave 8, phase 1; their buffer last held chunk c - 1), and the
 // second half of the queries and the value slice of chunk c + 1 (phase 2; every reader of those
 // buffers runs in phase 1).
-template <bool RAW>
+template <bool RAW, bool L2N>
 __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, const Stream& str, int c0, int l,
                                               int64_t nchunks) {
   const int64_t tok0 = str.tok, T = str.T;
@@ -582,7 +640,7 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, cons
     uint32_t bb, gg;
     v4u vv[4];
   };
-  RowStage<1> qa(p.q, str, l), qb(p.q, str, l);
+  RowStage<1, L2N> qa(p.q, str, l), qb(p.q, str, l);
   Set sa, sb;
   auto load_g = [&](Set& st, int64_t t0) {
     st.bb = __builtin_amdgcn_raw_buffer_load_b16(br, (int)((t0 + l) * 2), 0, 0);
@@ -607,7 +665,8 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, cons
     Aexp = __expf(p.A_log[h]);
     dtb = p.dt_bias[h];
   }
-  auto iter = [&](int c, Set& st, RowStage<1>& qs) {
+  auto iter = [&](int c, Set& st, RowStage<1, L2N>& qs) {
+    float dl, bgam;  // e^{G_63 - G_l} and beta gamma of chunk c + 2, scaled by 1 / |k_l| in phase 2 with L2N
     {
       float g = bf16_bits_to_f32(st.gg & 0xffffu), bt = bf16_bits_to_f32(st.bb & 0xffffu);
       if constexpr (RAW) {
@@ -627,7 +686,9 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, cons
       const float gam = __expf(x), el = __expf(x - gref);
       gt.G[l] = x;
       gt.gam[l] = gam;
-      gt.dec[l] = __expf(glast - x);
+      dl = __expf(glast - x);
+      bgam = beta * gam;
+      if constexpr (!L2N) gt.dec[l] = dl;
       gt.beta[l] = beta;
       gt.el[l] = el;
       gt.nbel[l] = -beta * el;
@@ -635,12 +696,18 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, cons
       gt.er[1][l] = __expf(fminf(gr2 - x, 0.f));
       gt.er[2][l] = __expf(fminf(gr3 - x, 0.f));
       gt.bbg[l][0] = (_Float16)beta;
-      gt.bbg[l][1] = (_Float16)(beta * gam);
+      if constexpr (!L2N) gt.bbg[l][1] = (_Float16)bgam;
       load_g(st, (int64_t)(c + 4) * C);
     }
     __syncthreads();
-    qs.store(sm.q);
+    qs.store(sm.q, sm.rq);
     qs.load((int64_t)(c + 3) * C);
+    if constexpr (L2N) {  // the key norms of chunk c + 2 were staged in phase 1
+      Gates& gt = sm.gt[kbuf(c + 2)];
+      const float r = gt.rk[l];
+      gt.dec[l] = dl * r;
+      gt.bbg[l][1] = (_Float16)(bgam * r);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {  // value channel 8 dq + e: tokens 4 vq .. 4 vq + 3 (bf16 bits)
       uint2 o;
@@ -659,13 +726,14 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, cons
 }
 
 // Role: first half of the queries of chunk c + 1 (wave 9, phase 2), loaded two iterations ahead.
+template <bool L2N>
 __device__ __forceinline__ void q_role(Smem& sm, const ChunkArgs& p, const Stream& str, int l, int64_t nchunks) {
-  RowStage<0> qa(p.q, str, l), qb(p.q, str, l);
+  RowStage<0, L2N> qa(p.q, str, l), qb(p.q, str, l);
   qa.load(-C);
   qb.load(0);
-  auto iter = [&](int c, RowStage<0>& qs) {
+  auto iter = [&](int c, RowStage<0, L2N>& qs) {
     __syncthreads();
-    qs.store(sm.q);
+    qs.store(sm.q, sm.rq);
     qs.load((int64_t)(c + 3) * C);
     __syncthreads();
   };
@@ -679,7 +747,7 @@ __device__ __forceinline__ void q_role(Smem& sm, const ChunkArgs& p, const Strea
 // Role: half SET of the tiles of P = tril(Q K^T * D) of chunk c (waves 10, 11, phase 1; read by
 // the outputs in phase 2), and half SET of the off-diagonal blocks of -A of chunk c + 2
 // (phase 2; their keys and gates were staged in phase 1), used one iteration later.
-template <int SET>
+template <int SET, bool L2N>
 __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
   const int lr = l & 15, lg = l >> 4;
   // P tiles (R, J): set 0 = (0,0) (1,1) (1,0) (2,0) (3,0); set 1 = (2,2) (3,3) (2,1) (3,1) (3,2).
@@ -692,7 +760,7 @@ __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
   for (int c = -2; c < (int)nchunks; ++c) {
     {
       const Gates& g = sm.gt[kbuf(c)];
-      f4 fac[5], acc[5];
+      f4 fac[5], acc[5], rkc[5];
 #pragma unroll
       for (int t = 0; t < 5; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
       {
@@ -712,6 +780,12 @@ __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           if (kk < 3) ld(kk + 1, kf[(kk + 1) & 1], qf[(kk + 1) & 1]);
+          if constexpr (L2N) {  // unit keys: columns scale by 1 / |k_j| (rows by 1 / |q_r| at the outputs);
+            if (kk == 2) {      // read behind the last fragments so no fragment load waits for them
+#pragma unroll
+              for (int t = 0; t < 5; ++t) rkc[t] = *reinterpret_cast<const f4*>(&g.rk[16 * PJ[SET][t] + 4 * lg]);
+            }
+          }
           sched_fence();
 #pragma unroll
           for (int t = 0; t < 5; ++t) acc[t] = mfma32(kf[kk & 1][PJ[SET][t]], qf[kk & 1][PR[SET][t]], acc[t]);
@@ -719,14 +793,16 @@ __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
         }
       }
 #pragma unroll
-      for (int t = 0; t < 5; ++t)
+      for (int t = 0; t < 5; ++t) {
+        if constexpr (L2N) fac[t] *= rkc[t];
         *reinterpret_cast<h4*>(&sm.p[16 * PR[SET][t] + lr][16 * PJ[SET][t] + 4 * swl4(l)]) = to_h4(fac[t] * acc[t]);
+      }
     }
     __syncthreads();
     {
       const int kb2 = kbuf(c + 2), ab = (int)(c & 1);
       const Gates& g = sm.gt[kb2];
-      f4 fac[3], acc[3];
+      f4 fac[3], acc[3], rkc[3];
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         fac[t] = offdiag_neg_a(g, AR[SET][t], AJ[SET][t], lr, lg, f4{1.f, 1.f, 1.f, 1.f});
@@ -742,6 +818,13 @@ __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           if (kk < 3) ld(kk + 1, kf[(kk + 1) & 1]);
+          if constexpr (L2N) {  // unit keys: rows and columns scale by 1 / |k|, read behind the fragments
+            if (kk == 2) {
+#pragma unroll
+              for (int t = 0; t < 3; ++t)
+                rkc[t] = g.rk[16 * AR[SET][t] + lr] * *reinterpret_cast<const f4*>(&g.rk[16 * AJ[SET][t] + 4 * lg]);
+            }
+          }
           sched_fence();
 #pragma unroll
           for (int t = 0; t < 3; ++t) acc[t] = mfma32(kf[kk & 1][AJ[SET][t]], kf[kk & 1][AR[SET][t]], acc[t]);
@@ -749,14 +832,16 @@ __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
         }
       }
 #pragma unroll
-      for (int t = 0; t < 3; ++t)
+      for (int t = 0; t < 3; ++t) {
+        if constexpr (L2N) fac[t] *= rkc[t];
         *reinterpret_cast<h4*>(&sm.an[ab][an_idx(AR[SET][t], AJ[SET][t])][lr][4 * lg]) = to_h4(fac[t] * acc[t]);
+      }
     }
     __syncthreads();
   }
 }
 
-template <typename TOut, bool RAW>
+template <typename TOut, bool RAW, bool L2N>
 __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
@@ -800,16 +885,16 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
       __builtin_amdgcn_s_setprio(2);
       chain_role(sm, p, str, c0, w, l, nchunks);
       break;
-    case 2: tdiag_role<0>(sm, l, nchunks); break;
-    case 3: tdiag_role<2>(sm, l, nchunks); break;
-    case 4: out_role<TOut, 0>(sm, p, str, c0, l, nchunks); break;
-    case 5: out_role<TOut, 2>(sm, p, str, c0, l, nchunks); break;
-    case 6: key_toff_role<0>(sm, p, str, l, nchunks); break;
-    case 7: key_toff_role<1>(sm, p, str, l, nchunks); break;
-    case 8: gates_qv_role<RAW>(sm, p, str, c0, l, nchunks); break;
-    case 9: q_role(sm, p, str, l, nchunks); break;
-    case 10: pa_role<0>(sm, l, nchunks); break;
-    default: pa_role<1>(sm, l, nchunks); break;
+    case 2: tdiag_role<0, L2N>(sm, l, nchunks); break;
+    case 3: tdiag_role<2, L2N>(sm, l, nchunks); break;
+    case 4: out_role<TOut, 0, L2N>(sm, p, str, c0, l, nchunks); break;
+    case 5: out_role<TOut, 2, L2N>(sm, p, str, c0, l, nchunks); break;
+    case 6: key_toff_role<0, L2N>(sm, p, str, l, nchunks); break;
+    case 7: key_toff_role<1, L2N>(sm, p, str, l, nchunks); break;
+    case 8: gates_qv_role<RAW, L2N>(sm, p, str, c0, l, nchunks); break;
+    case 9: q_role<L2N>(sm, p, str, l, nchunks); break;
+    case 10: pa_role<0, L2N>(sm, l, nchunks); break;
+    default: pa_role<1, L2N>(sm, l, nchunks); break;
   }
 }
 
@@ -820,18 +905,24 @@ bool chunk_mfma_supported(const ChunkArgs& a) {
   return a.in_dtype == GDN_BF16 && a.D == D && a.chunk == C && a.T * D * 4 < (INT64_C(1) << 31);
 }
 
+template <typename TOut>
+void launch_variant(const ChunkArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.raw_gates) {
+    if (a.qk_l2norm) hipLaunchKernelGGL((gdn_chunk_mfma_kernel<TOut, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gdn_chunk_mfma_kernel<TOut, true, false>), grid, block, 0, s, a);
+  } else {
+    if (a.qk_l2norm) hipLaunchKernelGGL((gdn_chunk_mfma_kernel<TOut, false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gdn_chunk_mfma_kernel<TOut, false, false>), grid, block, 0, s, a);
+  }
+}
+
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool kda, hipStream_t s) {
   if (kda) return launch_kda_mfma(a, s);
   const int64_t blocks = a.B * a.H * NT;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(NTH);
-  if (a.out_dtype == GDN_BF16) {
-    if (a.raw_gates) hipLaunchKernelGGL((gdn_chunk_mfma_kernel<__hip_bfloat16, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gdn_chunk_mfma_kernel<__hip_bfloat16, false>), grid, block, 0, s, a);
-  } else {
-    if (a.raw_gates) hipLaunchKernelGGL((gdn_chunk_mfma_kernel<float, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((gdn_chunk_mfma_kernel<float, false>), grid, block, 0, s, a);
-  }
+  if (a.out_dtype == GDN_BF16) launch_variant<__hip_bfloat16>(a, grid, block, s);
+  else launch_variant<float>(a, grid, block, s);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ struct ChunkArgs {
   // layer prologue (gdn_chunk_fwd_ex; matrix-core path only)
   int64_t Hqk;             // query/key heads (H a multiple); equals H for the plain entry points
   int raw_gates;           // beta / log_alpha carry the raw b / a projections
+  int qk_l2norm;           // q and k rows are scaled to unit length in the kernel
   const float *A_log, *dt_bias;  // [H], raw gates only
   const int32_t* cu_seqlens;     // [B + 1] token offsets of a ragged batch (T = total), or null
 };

@@ -183,13 +183,17 @@ def make_serving(N: int, T: int, H: int, Hqk: int, D: int, P: int, dtype: torch.
 
 
 def make_prefill_ex(B: int, H: int, Hqk: int, T: int, D: int, dtype: torch.dtype = torch.bfloat16, *,
-                    raw: bool = False, s0_std: float = 0.01, seed: int = 0) -> Dict[str, Optional[torch.Tensor]]:
+                    raw: bool = False, unit: bool = True, s0_std: float = 0.01,
+                    seed: int = 0) -> Dict[str, Optional[torch.Tensor]]:
     """Prefill inputs with H value heads reading Hqk query/key heads, drawn in the order q, k,
-    v, gates, s0 (and A_log, dt_bias for raw gates): q, k [B, Hqk, T, D] of unit length,
-    v [B, H, T, D]; the gates as in ``make_serving``."""
+    v, gates, s0 (and A_log, dt_bias for raw gates): q, k [B, Hqk, T, D] ~ N(0, 1), scaled to
+    unit length unless ``unit`` is False (the layer's unnormalised projections), v [B, H, T, D];
+    the gates as in ``make_serving``."""
     g = torch.Generator("cpu").manual_seed(seed)
-    q = _unit(torch.randn(B, Hqk, T, D, generator=g))
-    k = _unit(torch.randn(B, Hqk, T, D, generator=g))
+    q = torch.randn(B, Hqk, T, D, generator=g)
+    k = torch.randn(B, Hqk, T, D, generator=g)
+    if unit:
+        q, k = _unit(q), _unit(k)
     v = torch.randn(B, H, T, D, generator=g)
     A_log = dt_bias = None
     if raw:

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 110 /* 1.1.0 */
+#define GDN_VERSION 111 /* 1.1.1 */
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
 
@@ -145,15 +145,18 @@ gdn_status_t kda_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void*
  *   cu_seqlens [B + 1] int32 device array, non-decreasing from 0 to T, or NULL.  Values out
  *             of that order are clamped into [0, T] (a sequence can come out empty), never
  *             used to address outside the tensors.  Snapshots need ckpt_every = 0 here.
+ *  - qk_l2norm = 1: every query and key row is scaled to unit length before use,
+ *    x / sqrt(sum(x^2) + 1e-6) over its Dk channels ("Attention, Part 4", section 6: the
+ *    layer normalises q and k before the memory step); qk_l2norm = 0 uses them as given.
  * Supported on the matrix-core path (bf16 inputs, Dk = Dv = 128, chunk = 64); with
- * H_qk = H, raw_gates = 0 and no cu_seqlens every combination gdn_chunk_fwd supports.  q and k are used
- * as given: normalise them before the call.  `reserved` must be 0.
+ * H_qk = H, raw_gates = 0, qk_l2norm = 0 and no cu_seqlens every combination gdn_chunk_fwd
+ * supports.
  */
 typedef struct {
   gdn_chunk_desc_t base;
   int64_t H_qk;
   int32_t raw_gates;
-  int32_t reserved;
+  int32_t qk_l2norm;
 } gdn_chunk_ex_desc_t;
 
 gdn_status_t gdn_chunk_fwd_ex(const gdn_chunk_ex_desc_t* d, const void* q, const void* k, const void* v,

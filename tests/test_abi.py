@@ -43,7 +43,7 @@ def test_desc_struct_layout(g):
 
 
 def test_version_and_status_strings(g):
-    assert g.gdn_version() == 110
+    assert g.gdn_version() == 111
     for s in range(4):
         assert isinstance(g.gdn_status_string(s), str) and g.gdn_status_string(s)
     assert g.gdn_status_string(99) == "unknown status"
@@ -177,11 +177,12 @@ def test_chunk_ex_validation_errors(g):
             q[int(i[1:])] = val
         return f(None if d is None else ctypes.byref(d), *q, None)
 
-    def ex(h_qk=2, raw=0, reserved=0, **kw):
-        return g.GdnChunkExDesc(_desc(g, H=4, **kw), h_qk, raw, reserved)
+    def ex(h_qk=2, raw=0, l2=0, **kw):
+        return g.GdnChunkExDesc(_desc(g, H=4, **kw), h_qk, raw, l2)
 
     assert call(None) == INV
-    assert call(ex(reserved=1)) == INV
+    assert call(ex(l2=2)) == INV
+    assert call(ex(h_qk=4, l2=1, in_dtype=g.GDN_F32, Dk=16, Dv=16, chunk=16)) == NS   # normalisation: matrix cores
     assert call(ex(h_qk=3)) == INV                        # H = 4 not a multiple of 3
     assert call(ex(h_qk=0)) == INV
     assert call(ex(raw=2)) == INV

@@ -43,6 +43,52 @@ def test_chunk_ex_small(T, raw, out_f32):
         assert rel_l2(sc, sc_ref) <= 2e-3
 
 
+@pytest.mark.parametrize("T", [64, 200])
+@pytest.mark.parametrize("raw", [False, True])
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_chunk_ex_l2norm(T, raw, out_f32):
+    """Unnormalised q, k (the layer's projections, rows of length about 11) normalised in the
+    kernel, against the oracle's normalisation in fp64."""
+    import gated_deltanet_state_amd as g
+    B, H, Hqk, D = 2, 4, 2, 128
+    say(f"chunk_ex l2norm T={T} raw={raw} out_f32={out_f32}")
+    inp = synth.make_prefill_ex(B, H, Hqk, T, D, raw=raw, unit=False, seed=300 + T + raw)
+    d = _cuda(inp)
+    o, sf, _ = g.gdn_chunk_fwd_ex(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["s0"], A_log=d["A_log"],
+                                  dt_bias=d["dt_bias"], qk_l2norm=True,
+                                  out_dtype=torch.float32 if out_f32 else None)
+    torch.cuda.synchronize()
+    o_ref, sf_ref, _ = serving.forward_ex(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], inp["s0"],
+                                          raw_gates=raw, A_log=inp["A_log"], dt_bias=inp["dt_bias"],
+                                          qk_l2norm=True)
+    assert rel_l2(o, o_ref) <= (1e-3 if out_f32 else 2e-3)
+    assert rel_l2(sf, sf_ref) <= 2e-3
+
+
+def test_chunk_ex_l2norm_scale_invariant():
+    """Scaling q and k rows by powers of two (exact in bf16) leaves the normalised prefill
+    unchanged up to the epsilon, and the unnormalised one not."""
+    import gated_deltanet_state_amd as g
+    B, H, T, D = 1, 4, 256, 128
+    inp = _cuda(synth.make_prefill_ex(B, H, H, T, D, unit=False, seed=31))
+    gen = torch.Generator("cpu").manual_seed(5)
+    sq = (2.0 ** torch.randint(-3, 4, (B, H, T, 1), generator=gen)).to(torch.bfloat16).cuda()
+    sk = (2.0 ** torch.randint(-3, 4, (B, H, T, 1), generator=gen)).to(torch.bfloat16).cuda()
+    run = lambda q, k, l2: g.gdn_chunk_fwd_ex(q, k, inp["v"], inp["beta"], inp["log_alpha"], inp["s0"],
+                                              qk_l2norm=l2, out_dtype=torch.float32)
+    a, b = run(inp["q"], inp["k"], True), run(inp["q"] * sq, inp["k"] * sk, True)
+    torch.cuda.synchronize()
+    # the epsilon and fp16 rounding of the normalised rows leave differences far below 1e-4
+    assert rel_l2(a[0], b[0]) <= 1e-4 and rel_l2(a[1], b[1]) <= 1e-4
+    # without the normalisation the outputs follow the scale of q (keys of unit length here:
+    # unnormalised keys of length ~11 make the recurrence diverge)
+    kf = inp["k"].float()
+    kn = (kf / kf.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    c, e = run(inp["q"] * sq, kn, False)[0], run(inp["q"], kn, False)[0]
+    torch.cuda.synchronize()
+    assert rel_l2(c, e) > 0.1
+
+
 def test_chunk_ex_plain_is_chunk_fwd():
     """H_qk = H and no raw gates: bit-identical to gdn_chunk_fwd."""
     import gated_deltanet_state_amd as g
@@ -53,31 +99,33 @@ def test_chunk_ex_plain_is_chunk_fwd():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_chunk_ex_grouped_32_16_heads():
-    """The published 32 value / 16 query-key head layout, raw gates, T = 1024, all heads."""
+@pytest.mark.parametrize("l2", [False, True])
+def test_chunk_ex_grouped_32_16_heads(l2):
+    """The published 32 value / 16 query-key head layout, raw gates (and, with l2, the q/k
+    normalisation: the whole layer prologue), T = 1024, all heads."""
     import gated_deltanet_state_amd as g
     B, H, Hqk, T, D = 1, 32, 16, 1024, 128
-    say("chunk_ex 32/16 heads T=1024 raw gates")
-    inp = synth.make_prefill_ex(B, H, Hqk, T, D, raw=True, seed=77)
+    say(f"chunk_ex 32/16 heads T=1024 raw gates l2={l2}")
+    inp = synth.make_prefill_ex(B, H, Hqk, T, D, raw=True, unit=not l2, seed=77)
     d = _cuda(inp)
     o, sf, _ = g.gdn_chunk_fwd_ex(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["s0"], A_log=d["A_log"],
-                                  dt_bias=d["dt_bias"], out_dtype=torch.float32)
+                                  dt_bias=d["dt_bias"], qk_l2norm=l2, out_dtype=torch.float32)
     torch.cuda.synchronize()
     o_ref, sf_ref, _ = serving.forward_ex(inp["q"], inp["k"], inp["v"], inp["beta"], inp["log_alpha"], inp["s0"],
-                                          raw_gates=True, A_log=inp["A_log"], dt_bias=inp["dt_bias"])
+                                          raw_gates=True, A_log=inp["A_log"], dt_bias=inp["dt_bias"], qk_l2norm=l2)
     assert rel_l2(o, o_ref) <= 1e-3
     assert rel_l2(sf, sf_ref) <= 2e-3
 
 
-@pytest.mark.parametrize("raw", [False, True])
-def test_ragged_batch(raw):
+@pytest.mark.parametrize("raw,l2", [(False, False), (True, False), (True, True)])
+def test_ragged_batch(raw, l2):
     """Six sequences of lengths 130, 64, 1, 0, 200, 65 (ragged tails, a single token, an empty
     one) prefilled in one call; per-sequence outputs and final states against the oracle."""
     import gated_deltanet_state_amd as g
     lens = [130, 64, 1, 0, 200, 65]
     B, H, Hqk, D = len(lens), 4, 2, 128
-    say(f"ragged batch raw={raw}")
-    seqs = [synth.make_prefill_ex(1, H, Hqk, n, D, raw=raw, seed=100 + i) for i, n in enumerate(lens)]
+    say(f"ragged batch raw={raw} l2={l2}")
+    seqs = [synth.make_prefill_ex(1, H, Hqk, n, D, raw=raw, unit=not l2, seed=100 + i) for i, n in enumerate(lens)]
     cat = lambda key, heads: torch.cat([s_[key][0].reshape(heads * s_[key].shape[2], *s_[key].shape[3:])
                                         for s_ in seqs], 0)
     q, k, v = cat("q", Hqk), cat("k", Hqk), cat("v", H)
@@ -87,10 +135,11 @@ def test_ragged_batch(raw):
     cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
     o, sf = g.gdn_chunk_fwd_ragged(q.cuda(), k.cuda(), v.cuda(), beta.cuda(), la.cuda(), cu.cuda(), H=H, H_qk=Hqk,
                                    s0=s0.cuda(), A_log=None if A_log is None else A_log.cuda(),
-                                   dt_bias=None if dt is None else dt.cuda(), out_dtype=torch.float32)
+                                   dt_bias=None if dt is None else dt.cuda(), qk_l2norm=l2,
+                                   out_dtype=torch.float32)
     torch.cuda.synchronize()
     o_ref, sf_ref = serving.forward_ragged(q, k, v, beta, la, cu, H=H, Hqk=Hqk, s0=s0, raw_gates=raw,
-                                           A_log=A_log, dt_bias=dt)
+                                           A_log=A_log, dt_bias=dt, qk_l2norm=l2)
     assert rel_l2(o, o_ref) <= 1e-3
     assert rel_l2(sf, sf_ref) <= 2e-3
     assert torch.equal(sf[3].cpu(), s0[3])   # the empty sequence keeps its state exactly
