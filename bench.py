@@ -241,8 +241,19 @@ def main():
             "ms": round(ms, 4), "Mtok_per_s": round(c.B * c.T / (ms * 1e-3) / 1e6, 3),
             "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
-        log(f"long prefill: {ms:.3f} ms")
-        del d, o, sf, sc
+        # the same with the snapshots written into pinned host memory by the kernel itself
+        sch = torch.empty(sc.shape, dtype=torch.float32, pin_memory=True)
+
+        def lstep_host(i):
+            g.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["s0"], chunk=c.chunk,
+                            ckpt_every=c.ckpt_every, o=o, s_final=sf, s_ckpt=sch)
+
+        ms_h = time_launches(lstep_host, 3, 1, torch)
+        extra["long_prefill"]["snapshots_to_host"] = {
+            "ms": round(ms_h, 4), "Mtok_per_s": round(c.B * c.T / (ms_h * 1e-3) / 1e6, 3),
+            "snapshot_MiB": round(sch.numel() * 4 / 2**20, 1)}
+        log(f"long prefill: {ms:.3f} ms; snapshots into pinned host memory: {ms_h:.3f} ms")
+        del d, o, sf, sc, sch
         torch.cuda.empty_cache()
 
     # ---------------- KDA prefill: B=2 H=32 T=8192 ----------------

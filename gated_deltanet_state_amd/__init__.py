@@ -123,6 +123,23 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(int(stream))
 
 
+def _ckpt_buffer(s_ckpt, shape, device, to_host: bool):
+    """The snapshot buffer: on the device, or in pinned host memory (written by the kernel
+    directly, see s_ckpt in include/gdn.h) when ``to_host`` or when a pinned CPU tensor is
+    passed."""
+    if s_ckpt is None:
+        if to_host:
+            return torch.empty(shape, dtype=torch.float32, pin_memory=True)
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if s_ckpt.device.type == "cpu":
+        if not s_ckpt.is_pinned():
+            raise ValueError("s_ckpt on the host must be pinned memory (pin_memory=True)")
+        _check(s_ckpt, "s_ckpt", shape, torch.float32, s_ckpt.device)
+    else:
+        _check(s_ckpt, "s_ckpt", shape, torch.float32, device)
+    return s_ckpt
+
+
 def _check(t: torch.Tensor, name: str, shape, dtype, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -152,7 +169,8 @@ def gdn_chunk_workspace_size(B: int, H: int, T: int, D: int, *, chunk: int = 64,
 
 
 def _chunk_fwd(kda: bool, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_dtype, o, s_final,
-               s_ckpt, return_final, stream) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
+               s_ckpt, return_final, stream,
+               snapshots_to_host: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, Dk]")
     B, H, T, D = q.shape
@@ -175,12 +193,7 @@ def _chunk_fwd(kda: bool, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_d
     if s_final is not None:
         _check(s_final, "s_final", (B, H, D, D), torch.float32, dev)
     n_ck = T // ckpt_every if ckpt_every > 0 else 0
-    if n_ck > 0:
-        if s_ckpt is None:
-            s_ckpt = torch.empty(B, H, n_ck, D, D, dtype=torch.float32, device=dev)
-        _check(s_ckpt, "s_ckpt", (B, H, n_ck, D, D), torch.float32, dev)
-    else:
-        s_ckpt = None
+    s_ckpt = _ckpt_buffer(s_ckpt, (B, H, n_ck, D, D), dev, snapshots_to_host) if n_ck > 0 else None
     d = _desc(B, H, T, D, chunk, in_dt, out_dt, ckpt_every)
     fn = lib.kda_chunk_fwd if kda else lib.gdn_chunk_fwd
     st = fn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(s0),
@@ -192,24 +205,26 @@ def _chunk_fwd(kda: bool, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_d
 
 def gdn_chunk_fwd(q, k, v, beta, log_alpha, s0=None, *, chunk: int = 64, ckpt_every: int = 0,
                   out_dtype=None, o=None, s_final=None, s_ckpt=None, return_final: bool = True,
-                  stream=None):
+                  stream=None, snapshots_to_host: bool = False):
     """Chunkwise prefill of the gated delta rule (see gdn_chunk_fwd in include/gdn.h).
 
     q, k [B,H,T,D]; v [B,H,T,D]; beta, log_alpha [B,H,T] (fp32 or bf16, one dtype);
     s0 [B,H,D,D] fp32 or None.  Returns (o [B,H,T,D], s_final [B,H,D,D] fp32 or None,
     s_ckpt [B,H,T//ckpt_every,D,D] fp32 or None).  Pass s_final=s0 to update in place.
-    Asynchronous on `stream` (default: torch's current stream).
+    Asynchronous on `stream` (default: torch's current stream).  With snapshots_to_host (or a
+    pinned CPU tensor as s_ckpt) the kernel writes the snapshots straight into pinned host
+    memory; read them after synchronising the stream.
     """
     return _chunk_fwd(False, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_dtype, o,
-                      s_final, s_ckpt, return_final, stream)
+                      s_final, s_ckpt, return_final, stream, snapshots_to_host)
 
 
 def kda_chunk_fwd(q, k, v, beta, log_alpha, s0=None, *, chunk: int = 64, ckpt_every: int = 0,
                   out_dtype=None, o=None, s_final=None, s_ckpt=None, return_final: bool = True,
-                  stream=None):
+                  stream=None, snapshots_to_host: bool = False):
     """Chunkwise prefill of KDA: as gdn_chunk_fwd with log_alpha [B,H,T,D] (one rate per key channel)."""
     return _chunk_fwd(True, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_dtype, o,
-                      s_final, s_ckpt, return_final, stream)
+                      s_final, s_ckpt, return_final, stream, snapshots_to_host)
 
 
 def gdn_decode_step(state, q, k, v, beta, log_alpha, *, o=None, out_dtype=None, stream=None):
@@ -291,7 +306,7 @@ def gdn_decode_commit(pool, q, k, v, beta, log_alpha, n_commit, **kw):
 
 def gdn_chunk_fwd_ex(q, k, v, beta, log_alpha, s0=None, *, A_log=None, dt_bias=None, qk_l2norm: bool = False,
                      chunk: int = 64, ckpt_every: int = 0, out_dtype=None, o=None, s_final=None, s_ckpt=None,
-                     return_final: bool = True, stream=None):
+                     return_final: bool = True, stream=None, snapshots_to_host: bool = False):
     """Chunkwise prefill with grouped query/key heads and optionally the raw gate projections
     and the q/k normalisation (gdn_chunk_fwd_ex in include/gdn.h).
 
@@ -325,12 +340,7 @@ def gdn_chunk_fwd_ex(q, k, v, beta, log_alpha, s0=None, *, A_log=None, dt_bias=N
     if s_final is not None:
         _check(s_final, "s_final", (B, H, D, D), torch.float32, dev)
     n_ck = T // ckpt_every if ckpt_every > 0 else 0
-    if n_ck > 0:
-        if s_ckpt is None:
-            s_ckpt = torch.empty(B, H, n_ck, D, D, dtype=torch.float32, device=dev)
-        _check(s_ckpt, "s_ckpt", (B, H, n_ck, D, D), torch.float32, dev)
-    else:
-        s_ckpt = None
+    s_ckpt = _ckpt_buffer(s_ckpt, (B, H, n_ck, D, D), dev, snapshots_to_host) if n_ck > 0 else None
     d = GdnChunkExDesc(_desc(B, H, T, D, chunk, in_dt, out_dt, ckpt_every), Hqk, int(raw), int(bool(qk_l2norm)))
     st = lib.gdn_chunk_fwd_ex(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
                               _ptr(A_log), _ptr(dt_bias), None, _ptr(s0), _ptr(o), _ptr(s_final), _ptr(s_ckpt),

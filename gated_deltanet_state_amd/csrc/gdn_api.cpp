@@ -115,6 +115,20 @@ gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, con
   if (s_final && !aligned16(s_final)) return GDN_ERROR_INVALID_VALUE;
   if (a.n_ckpt > 0) {
     if (!s_ckpt || !aligned16(s_ckpt)) return GDN_ERROR_INVALID_VALUE;
+    // Snapshots may go to pinned host memory: the kernel then writes each one into host RAM
+    // as it is reached, with no copy and no synchronisation.  Pageable host memory, which the
+    // GPU cannot write, is rejected; a pointer the runtime does not know is taken as device
+    // memory, as for every other argument.
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, s_ckpt) == hipSuccess) {
+      if (at.type == hipMemoryTypeUnregistered) return GDN_ERROR_INVALID_VALUE;
+      if (at.type == hipMemoryTypeHost) {
+        if (!at.devicePointer || !aligned16(at.devicePointer)) return GDN_ERROR_INVALID_VALUE;
+        s_ckpt = static_cast<float*>(at.devicePointer);
+      }
+    } else {
+      (void)hipGetLastError();  // the failed query must not be reported by the launch
+    }
   } else {
     s_ckpt = nullptr;
   }

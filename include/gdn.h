@@ -101,6 +101,13 @@ gdn_status_t gdn_chunk_workspace_size(const gdn_chunk_desc_t* d, int is_kda, siz
  *                             place); any other overlap with s0 is INVALID_VALUE.
  *   s_ckpt    [B, H, T / ckpt_every, Dv, Dk] fp32, written; required (non-NULL) when
  *                             ckpt_every > 0 and T >= ckpt_every, ignored otherwise.
+ *                             Device memory, or pinned host memory (hipHostMalloc): then
+ *                             every snapshot is written into host RAM by the kernel as soon
+ *                             as the prefill reaches it, so capturing snapshots needs no copy
+ *                             and never stalls the prefill ("Hybrid models...", same section,
+ *                             item 1: snapshot capture made asynchronous); the host may read
+ *                             them once the stream's work has completed.  Pageable host
+ *                             memory is INVALID_VALUE.
  *   workspace, workspace_bytes: at least gdn_chunk_workspace_size() bytes (NULL / 0 ok
  *                             when that is 0).
  * Supported: Dk == Dv; bf16 inputs with Dk = 128 and chunk = 64 run on the matrix
