@@ -299,16 +299,25 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
     }
     __syncthreads();
 
-    // ---- stage 2: add the sums of the earlier groups; publish G
-    if (tid < 256) {
-      float off[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int qg = 0; qg < rq; ++qg) {
+    // ---- stage 2a: exclusive prefix of the 16 group sums, two channels per lane of wave 4
+    if (w == 4) {
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      f2 x[16], run = {0.f, 0.f};
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const f4 x = *reinterpret_cast<const f4*>(&sm.pf.tot[qg][8 * g8 + 4 * h]);
-          off[4 * h] += x[0]; off[4 * h + 1] += x[1]; off[4 * h + 2] += x[2]; off[4 * h + 3] += x[3];
-        }
+      for (int qg = 0; qg < 16; ++qg) x[qg] = *reinterpret_cast<const f2*>(&sm.pf.tot[qg][2 * l]);
+#pragma unroll
+      for (int qg = 0; qg < 16; ++qg) {
+        *reinterpret_cast<f2*>(&sm.pf.tot[qg][2 * l]) = run;
+        run += x[qg];
       }
+    }
+    __syncthreads();
+
+    // ---- stage 2b: add the sums of the earlier groups; publish G
+    if (tid < 256) {
+      const f4 o0 = *reinterpret_cast<const f4*>(&sm.pf.tot[rq][8 * g8]);
+      const f4 o1 = *reinterpret_cast<const f4*>(&sm.pf.tot[rq][8 * g8 + 4]);
+      const float off[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -328,6 +337,14 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
       if (tid < 256) {
         const float* Ge = &sm.pf.G[16 * R + 15][8 * g8];
         const float* Gl = &sm.pf.G[C - 1][8 * g8];
+        // per channel: e^{G_end - G_m} and e^{G_63 - G_end} (both <= 1); per element one
+        // exponential and one reciprocal: e^{G_end - G_r} = e^{G_end - G_m} / e^{G_r - G_m}
+        float cem[8], c63[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          cem[e] = __expf(fminf(Ge[e] - Gm[e], 0.f));
+          c63[e] = __expf(fminf(Gl[e] - Ge[e], 0.f));
+        }
         h8 klh[4], kdh[4], krh[4], kth[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -335,11 +352,12 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
           for (int e = 0; e < 8; ++e) {
             const float k = bf_at(st.x[i], e);
             const float el = __expf(gl[i][e] - Gm[e]);          // e^{G_r - G_m}
-            const float er = __expf(fminf(Ge[e] - gl[i][e], 0.f));  // e^{G_end - G_r} <= 1
+            const float ie = __builtin_amdgcn_rcpf(el);          // e^{G_m - G_r}
+            const float er = fminf(cem[e] * ie, 1.f);            // e^{G_end - G_r} <= 1
             klh[i][e] = (_Float16)(k * el);
-            kdh[i][e] = (_Float16)(k * __frcp_rn(el));
+            kdh[i][e] = (_Float16)(k * ie);
             krh[i][e] = (_Float16)(k * er);
-            kth[i][e] = (_Float16)(k * er * __expf(fminf(Gl[e] - Ge[e], 0.f)));  // e^{G_63 - G_r}
+            kth[i][e] = (_Float16)(k * er * c63[e]);              // e^{G_63 - G_r}
           }
           const int row = 4 * rq + i;
           *reinterpret_cast<h8*>(&sm.kl[row][8 * g8]) = klh[i];
