@@ -841,6 +841,45 @@ __device__ __forceinline__ void pa_role(Smem& sm, int l, int64_t nchunks) {
   }
 }
 
+// A ragged batch is processed longest sequence first, so that the short ones fill in behind the
+// long ones instead of leaving a tail of long workgroups (workgroups are dispatched in id order,
+// round-robin over the XCDs).  Stream slot s (the workgroup id over NT, after the XCD remap) is
+// given the stream of dispatch rank r: the slot's position in dispatch order (round-robin over
+// the eight XCD groups of slots when the remap applies).  Rank r is value head r % H of the
+// sequence ranked r / H by length (descending, lower index first among equals).  Every slot
+// gets a distinct stream.  The lengths are ranked in the LDS of the P tile, before it is
+// cleared.  Needs B <= NTH; returns b * H + h of the slot's stream.
+__device__ __forceinline__ int64_t longest_first(Smem& sm, const ChunkArgs& p, int64_t slot, bool xcd_remap, int tid) {
+  const int64_t S = p.B * p.H;
+  const int64_t r = xcd_remap ? 8 * (slot % (S / 8)) + slot / (S / 8) : slot;
+  const int q = (int)(r / p.H);
+  int* len = reinterpret_cast<int*>(&sm.p[0][0]);  // NTH lengths (-1 past B), then the answer
+  int* win = len + NTH;
+  const int nb = (int)p.B, nb4 = (nb + 3) & ~3;
+  if (tid < nb) {
+    const int64_t t0 = min(max((int64_t)p.cu_seqlens[tid], (int64_t)0), p.T);
+    const int64_t t1 = min(max((int64_t)p.cu_seqlens[tid + 1], t0), p.T);
+    len[tid] = (int)(t1 - t0);
+  } else if (tid < nb4) {
+    len[tid] = -1;  // never longer than, nor equal to, a real length
+  }
+  __syncthreads();
+  if (tid < nb) {
+    const int lj = len[tid];
+    int rank = 0;
+    for (int i = 0; i < nb4; i += 4) {
+      const int4 l4 = *reinterpret_cast<const int4*>(&len[i]);
+      rank += (l4.x > lj || (l4.x == lj && i < tid)) + (l4.y > lj || (l4.y == lj && i + 1 < tid)) +
+              (l4.z > lj || (l4.z == lj && i + 2 < tid)) + (l4.w > lj || (l4.w == lj && i + 3 < tid));
+    }
+    if (rank == q) *win = tid;
+  }
+  __syncthreads();
+  const int64_t bh = (int64_t)(*win) * p.H + r % p.H;
+  __syncthreads();  // every wave has read the answer before the P tile is cleared
+  return bh;
+}
+
 template <typename TOut, bool RAW, bool L2N>
 __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
   __shared__ Smem sm;
@@ -852,9 +891,11 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
   // remap so the NT slices of a stream get ids that land on the same XCD.
   const unsigned nblk = gridDim.x;
   unsigned bid = blockIdx.x;
-  if (nblk % (8 * NT) == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
+  const bool xcd_remap = nblk % (8 * NT) == 0;
+  if (xcd_remap) bid = (bid % 8) * (nblk / 8) + bid / 8;
   const int c0 = (int)(bid % NT) * DVT;
-  const int64_t bh = bid / NT;
+  int64_t bh = bid / NT;
+  if (p.cu_seqlens && p.B <= NTH) bh = longest_first(sm, p, bh, xcd_remap, tid);
   // value head h of sequence b reads query/key head h / (H / Hqk)
   const int64_t b = bh / p.H, h = bh % p.H, hq = h / (p.H / p.Hqk);
   Stream str;
