@@ -202,3 +202,29 @@ def test_ragged_many_sequences_any_order():
     assert torch.equal(sf[5].cpu(), s0[5])
     for b in (0, 17, 39):   # per sequence too: a stream swapped with another would show here
         assert rel_l2(sf[b], sf_ref[b]) <= 2e-3
+
+
+@pytest.mark.parametrize("B,H,lo,hi", [(5, 3, 0, 200), (800, 2, 0, 5)])
+def test_ragged_dispatch_orders(B, H, lo, hi):
+    """B * H not a multiple of 8 (no XCD grouping of the slots) and B above the 768 sequences
+    the kernel ranks by length (dispatch in argument order): every stream still lands once."""
+    import gated_deltanet_state_amd as g
+    gen = torch.Generator("cpu").manual_seed(B + H)
+    lens = [int(x) for x in torch.randint(lo, hi + 1, (B,), generator=gen)]
+    Hqk, D = 1, 128
+    say(f"ragged B={B} H={H}")
+    seqs = [synth.make_prefill_ex(1, H, Hqk, n, D, s0_std=0.05, seed=900 + i) for i, n in enumerate(lens)]
+    cat = lambda key, heads: torch.cat([s_[key][0].reshape(heads * s_[key].shape[2], *s_[key].shape[3:])
+                                        for s_ in seqs], 0)
+    q, k, v = cat("q", Hqk), cat("k", Hqk), cat("v", H)
+    beta, la = cat("beta", H), cat("log_alpha", H)
+    s0 = torch.cat([s_["s0"] for s_ in seqs], 0)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    o, sf = g.gdn_chunk_fwd_ragged(q.cuda(), k.cuda(), v.cuda(), beta.cuda(), la.cuda(), cu.cuda(), H=H, H_qk=Hqk,
+                                   s0=s0.cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, sf_ref = serving.forward_ragged(q, k, v, beta, la, cu, H=H, Hqk=Hqk, s0=s0)
+    assert rel_l2(o, o_ref) <= 1e-3
+    assert rel_l2(sf, sf_ref) <= 2e-3
+    worst = max(rel_l2(sf[b], sf_ref[b]) for b in range(B))   # a swapped stream would stand out
+    assert worst <= 5e-3
