@@ -17,7 +17,8 @@
  *
  * Conventions shared by every entry point
  *  - Tensor pointers are DEVICE pointers to contiguous row-major arrays with the
- *    layouts given below; q, k, v, o, s0, s_final, s_ckpt and state must be 16-byte
+ *    layouts given below (the prefill's s_ckpt may also be pinned host memory, see
+ *    gdn_chunk_fwd); q, k, v, o, s0, s_final, s_ckpt and state must be 16-byte
  *    aligned.  `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *  - The caller owns every buffer.  The library allocates nothing, frees nothing and
  *    keeps no pointer after a call returns.  Outputs are overwritten entirely.
@@ -29,8 +30,9 @@
  *  - Device VALUES are not checked.  Preconditions: log_alpha finite and <= 0
  *    (alpha in (0, 1]); beta finite (in (0, 1) on the pages); |q|, |k|, |v| <= 65504
  *    for bf16 inputs (the prefill kernels use half-precision matrix-core operands).
- *    Queries and keys are expected to be L2-normalised by the caller (the core does
- *    not normalise and applies no 1/sqrt(d) scale), but this is not required.
+ *    Queries and keys are expected to be L2-normalised by the caller (the plain entry
+ *    points do not normalise; gdn_chunk_fwd_ex and gdn_decode_ex can, with qk_l2norm),
+ *    but this is not required.  No 1/sqrt(d) scale is applied.
  *    Invalid values give NaN/Inf in the outputs, never a fault.
  */
 #ifndef GDN_H
