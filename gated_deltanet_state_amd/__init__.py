@@ -170,7 +170,7 @@ def gdn_chunk_workspace_size(B: int, H: int, T: int, D: int, *, chunk: int = 64,
 
 def _chunk_fwd(kda: bool, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_dtype, o, s_final,
                s_ckpt, return_final, stream,
-               snapshots_to_host: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
+               snapshots_to_host: bool = False, workspace=None) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, Dk]")
     B, H, T, D = q.shape
@@ -196,8 +196,19 @@ def _chunk_fwd(kda: bool, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_d
     s_ckpt = _ckpt_buffer(s_ckpt, (B, H, n_ck, D, D), dev, snapshots_to_host) if n_ck > 0 else None
     d = _desc(B, H, T, D, chunk, in_dt, out_dt, ckpt_every)
     fn = lib.kda_chunk_fwd if kda else lib.gdn_chunk_fwd
+    # the matrix-core KDA prefill runs in its two-kernel form when given its workspace
+    ws, ws_bytes = None, 0
+    if workspace is not False:
+        need = ctypes.c_size_t(0)
+        st = lib.gdn_chunk_workspace_size(ctypes.byref(d), int(kda), ctypes.byref(need))
+        if st != GDN_SUCCESS:
+            raise GdnError(st, "gdn_chunk_workspace_size")
+        if need.value > 0:
+            if workspace is None:
+                workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+            ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
     st = fn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(s0),
-            _ptr(o), _ptr(s_final), _ptr(s_ckpt), None, 0, _stream(stream))
+            _ptr(o), _ptr(s_final), _ptr(s_ckpt), _ptr(ws), ws_bytes, _stream(stream))
     if st != GDN_SUCCESS:
         raise GdnError(st, "kda_chunk_fwd" if kda else "gdn_chunk_fwd")
     return o, s_final, s_ckpt
@@ -221,10 +232,14 @@ def gdn_chunk_fwd(q, k, v, beta, log_alpha, s0=None, *, chunk: int = 64, ckpt_ev
 
 def kda_chunk_fwd(q, k, v, beta, log_alpha, s0=None, *, chunk: int = 64, ckpt_every: int = 0,
                   out_dtype=None, o=None, s_final=None, s_ckpt=None, return_final: bool = True,
-                  stream=None, snapshots_to_host: bool = False):
-    """Chunkwise prefill of KDA: as gdn_chunk_fwd with log_alpha [B,H,T,D] (one rate per key channel)."""
+                  stream=None, snapshots_to_host: bool = False, workspace=None):
+    """Chunkwise prefill of KDA: as gdn_chunk_fwd with log_alpha [B,H,T,D] (one rate per key channel).
+
+    workspace: None (default) allocates the device workspace of the two-kernel form through
+    torch when the matrix-core path applies (gdn_chunk_workspace_size bytes); a uint8 device
+    tensor of at least that size is used as given; False runs the single-kernel form."""
     return _chunk_fwd(True, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_dtype, o,
-                      s_final, s_ckpt, return_final, stream, snapshots_to_host)
+                      s_final, s_ckpt, return_final, stream, snapshots_to_host, workspace)
 
 
 def gdn_decode_step(state, q, k, v, beta, log_alpha, *, o=None, out_dtype=None, stream=None):

@@ -94,8 +94,14 @@ gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, con
     a.A_log = pro->raw_gates ? pro->A_log : nullptr;
     a.dt_bias = pro->raw_gates ? pro->dt_bias : nullptr;
   }
-  (void)workspace;
-  (void)workspace_bytes;  // the fused kernels need no workspace (size 0)
+  // Only the matrix-core KDA prefill takes a workspace (its two-kernel form); without one it
+  // runs as a single kernel.  A workspace that is given must be large enough.
+  if (workspace && is_kda && gdn::chunk_mfma_supported(a) && a.T > 0) {
+    const size_t need = gdn::kda_workspace_bytes(a);
+    if (workspace_bytes < need || !aligned16(workspace)) return GDN_ERROR_INVALID_VALUE;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+  }
   const int64_t BH = a.B * a.H;
   if (BH == 0) return GDN_SUCCESS;
   const size_t state_bytes = (size_t)BH * (size_t)(a.D * a.D) * sizeof(float);
@@ -145,6 +151,11 @@ gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, con
   if (o && (overlaps(o, o_bytes, s0, s0 ? state_bytes : 0) ||
             overlaps(o, o_bytes, s_final, s_final ? state_bytes : 0)))
     return GDN_ERROR_INVALID_VALUE;
+  if (a.workspace && (overlaps(a.workspace, a.workspace_bytes, o, o_bytes) ||
+                      overlaps(a.workspace, a.workspace_bytes, s_final, s_final ? state_bytes : 0) ||
+                      overlaps(a.workspace, a.workspace_bytes, s0, s0 ? state_bytes : 0) ||
+                      overlaps(a.workspace, a.workspace_bytes, s_ckpt, s_ckpt ? ck_bytes : 0)))
+    return GDN_ERROR_INVALID_VALUE;
   (void)in_elem;
 
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
@@ -164,7 +175,7 @@ gdn_status_t gdn_chunk_workspace_size(const gdn_chunk_desc_t* d, int is_kda, siz
   gdn::ChunkArgs a;
   gdn_status_t st = check_chunk_desc(d, is_kda, &a);
   if (st != GDN_SUCCESS) return st;
-  *bytes = 0;
+  *bytes = (is_kda && gdn::chunk_mfma_supported(a)) ? gdn::kda_workspace_bytes(a) : 0;
   return GDN_SUCCESS;
 }
 

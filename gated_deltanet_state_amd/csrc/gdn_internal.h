@@ -27,6 +27,8 @@ struct ChunkArgs {
   int qk_l2norm;           // q and k rows are scaled to unit length in the kernel
   const float *A_log, *dt_bias;  // [H], raw gates only
   const int32_t* cu_seqlens;     // [B + 1] token offsets of a ragged batch (T = total), or null
+  void* workspace;               // caller's device workspace (KDA two-kernel form), or null
+  size_t workspace_bytes;
 };
 
 struct DecodeArgs {
@@ -54,6 +56,8 @@ struct DecodeExArgs {
 bool chunk_mfma_supported(const ChunkArgs& a);
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool kda, hipStream_t stream);
 hipError_t launch_kda_mfma(const ChunkArgs& a, hipStream_t stream);
+// Workspace of the two-kernel matrix-core KDA prefill: one 64 KiB record per (stream, chunk).
+size_t kda_workspace_bytes(const ChunkArgs& a);
 
 // fp32 vector-unit prefill (fp32 or bf16 inputs, D in {16,32,64,128}, chunk in {16,32,64}).
 bool chunk_valu_supported(const ChunkArgs& a);

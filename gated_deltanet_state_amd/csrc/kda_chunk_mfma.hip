@@ -167,7 +167,7 @@ struct Jobs {
 };
 
 // Gram / score tile (M = j, N = r): the lane holds r = 16 R + lr, j = 16 J + 4 lg + i.
-template <class L>
+template <class L, bool PRESCALED = false>
 __device__ __forceinline__ void produce(Smem& sm, int l, f4* Oacc) {
   const int lr = l & 15, lg = l >> 4;
   f4 acc[5];
@@ -182,7 +182,8 @@ __device__ __forceinline__ void produce(Smem& sm, int l, f4* Oacc) {
       if (jb == kNone) continue;
       const int kind = jb >> 4, R = (jb >> 2) & 3, J = jb & 3;
       if (kind == 2) {  // O^T[dv][c] += sum S[dv][ch] (Q Gamma)[c][ch]: B operand = ql rows c * e^{G_m(R)}
-        const h8 qb = scale8(frag8(&sm.ql[0][0], LQ, 16 * R, 32 * kk, l), &sm.tb.em[R][ch]);
+        const h8 qf = frag8(&sm.ql[0][0], LQ, 16 * R, 32 * kk, l);
+        const h8 qb = PRESCALED ? qf : scale8(qf, &sm.tb.em[R][ch]);
         acc[t] = mfma32(frag8(&sm.s[0][0], LQ, 16 * J, 32 * kk, l), qb, acc[t]);
       } else {
         const _Float16* Am = (R == J) ? &sm.kd[0][0] : &sm.kr[0][0];
@@ -241,8 +242,283 @@ __device__ __forceinline__ void o_tile(int w, int t, int& cb, int& db) {
   db = idx & 1;
 }
 
-template <typename TOut>
-__global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
+// Stages one chunk (ends with a barrier): the per-channel prefix of log alpha (stage 1, 2a,
+// 2b), then the scaled operand tiles, the per-channel tables, the value slice and beta
+// (stage 3) from the registers of stage_load.  Every thread of the workgroup calls it.
+__device__ __forceinline__ void stage_chunk(Smem& sm, const Stage& st, int tid, int w, int l) {
+  const int t = tid & 255, g8 = t & 15, rq = t >> 4;
+  // ---- stage 1: per-channel prefix of log alpha over each group of 4 tokens
+  float gl[4][8];
+  if (tid < 256) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a += bf_at(st.g[i], e);
+        gl[i][e] = a;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<f4*>(&sm.pf.tot[rq][8 * g8 + 4 * h]) = f4{gl[3][4 * h], gl[3][4 * h + 1], gl[3][4 * h + 2], gl[3][4 * h + 3]};
+  }
+  __syncthreads();
+
+  // ---- stage 2a: exclusive prefix of the 16 group sums, two channels per lane of wave 4
+  if (w == 4) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    f2 x[16], run = {0.f, 0.f};
+#pragma unroll
+    for (int qg = 0; qg < 16; ++qg) x[qg] = *reinterpret_cast<const f2*>(&sm.pf.tot[qg][2 * l]);
+#pragma unroll
+    for (int qg = 0; qg < 16; ++qg) {
+      *reinterpret_cast<f2*>(&sm.pf.tot[qg][2 * l]) = run;
+      run += x[qg];
+    }
+  }
+  __syncthreads();
+
+  // ---- stage 2b: add the sums of the earlier groups; publish G
+  if (tid < 256) {
+    const f4 o0 = *reinterpret_cast<const f4*>(&sm.pf.tot[rq][8 * g8]);
+    const f4 o1 = *reinterpret_cast<const f4*>(&sm.pf.tot[rq][8 * g8 + 4]);
+    const float off[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gl[i][e] += off[e];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<f4*>(&sm.pf.G[4 * rq + i][8 * g8 + 4 * h]) =
+            f4{gl[i][4 * h], gl[i][4 * h + 1], gl[i][4 * h + 2], gl[i][4 * h + 3]};
+    }
+  }
+  __syncthreads();
+
+  // ---- stage 3: scaled operand tiles, tables, values, beta
+  {
+    const int R = rq >> 2;  // block of this thread's 4 tokens
+    const float* Gm = &sm.pf.G[16 * R + 7][8 * g8];
+    if (tid < 256) {
+      const float* Ge = &sm.pf.G[16 * R + 15][8 * g8];
+      const float* Gl = &sm.pf.G[C - 1][8 * g8];
+      // per channel: e^{G_end - G_m} and e^{G_63 - G_end} (both <= 1); per element one
+      // exponential and one reciprocal: e^{G_end - G_r} = e^{G_end - G_m} / e^{G_r - G_m}
+      float cem[8], c63[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cem[e] = __expf(fminf(Ge[e] - Gm[e], 0.f));
+        c63[e] = __expf(fminf(Gl[e] - Ge[e], 0.f));
+      }
+      h8 klh[4], kdh[4], krh[4], kth[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float k = bf_at(st.x[i], e);
+          const float el = __expf(gl[i][e] - Gm[e]);          // e^{G_r - G_m}
+          const float ie = __builtin_amdgcn_rcpf(el);          // e^{G_m - G_r}
+          const float er = fminf(cem[e] * ie, 1.f);            // e^{G_end - G_r} <= 1
+          klh[i][e] = (_Float16)(k * el);
+          kdh[i][e] = (_Float16)(k * ie);
+          krh[i][e] = (_Float16)(k * er);
+          kth[i][e] = (_Float16)(k * er * c63[e]);              // e^{G_63 - G_r}
+        }
+        const int row = 4 * rq + i;
+        *reinterpret_cast<h8*>(&sm.kl[row][8 * g8]) = klh[i];
+        *reinterpret_cast<h8*>(&sm.kd[row][8 * g8]) = kdh[i];
+        *reinterpret_cast<h8*>(&sm.kr[row][8 * g8]) = krh[i];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        h4 col;
+        col[0] = kth[0][e]; col[1] = kth[1][e]; col[2] = kth[2][e]; col[3] = kth[3][e];
+        *reinterpret_cast<h4*>(&sm.kt[8 * g8 + e][kt_col(8 * g8 + e, 4 * rq)]) = col;
+      }
+      *reinterpret_cast<h8*>(&sm.v[t >> 2][8 * (t & 3)]) = bf8_to_h8(st.v);
+      if (tid < C) sm.tb.beta[tid] = __uint_as_float(static_cast<uint32_t>(st.beta) << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float* Gr = &sm.pf.G[4 * rq + i][8 * g8];
+        h8 qh;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qh[e] = (_Float16)(bf_at(st.x[i], e) * __expf(Gr[e] - Gm[e]));
+        *reinterpret_cast<h8*>(&sm.ql[4 * rq + i][8 * g8]) = qh;
+      }
+      if (tid >= 384) {  // tables, one channel per thread
+        const int ch = tid - 384;
+#pragma unroll
+        for (int R2 = 0; R2 < 4; ++R2) {
+          const float gm = sm.pf.G[16 * R2 + 7][ch];
+          sm.tb.em[R2][ch] = __expf(gm);
+#pragma unroll
+          for (int J2 = 0; J2 < R2; ++J2) sm.tb.fm[R2][J2][ch] = __expf(fminf(gm - sm.pf.G[16 * J2 + 15][ch], 0.f));
+        }
+        sm.tb.gc[ch] = __expf(sm.pf.G[C - 1][ch]);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------
+// Two-kernel form (used when the caller provides the workspace).  Everything a chunk needs
+// that does not depend on the state -- the staged operand tiles, P, -A and the inverses of
+// the diagonal blocks of (I + A), the per-channel tables -- is computed once per (stream,
+// chunk) by kda_prep_kernel, fully in parallel, into one record of the workspace.  The
+// sequential kernel then only stages a record per chunk (plain copies, one chunk ahead) and
+// runs X, the substitution, the outputs and the state hand-off.  The single kernel recomputes
+// that state-independent work in each of the NT workgroups of a stream, one chunk after
+// another.  Both forms run the same arithmetic on the same operands.
+struct KdaRec {
+  _Float16 kl[C][D];       // k_r e^{G_r - G_m(R)} e^{G_m(R)}, rounded as the single kernel rounds it at use
+  _Float16 ql[C][D];       // q_r e^{G_r - G_m(R)} e^{G_m(R)}, likewise
+  _Float16 kt[D][C];       // k_c e^{G_63 - G_c}, [d_k][token]
+  _Float16 p[C][C];        // tril((Q*Gamma)(K/Gamma)^T), zero above the diagonal blocks
+  _Float16 an[6][16][16];  // -A, blocks (R, J), R > J, in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+  _Float16 td[4][16][16];  // inverses of the diagonal blocks of (I + A), row-major
+  float em[4][D];          // e^{G_m(R)}
+  float gc[D];             // e^{G_63}
+  float beta[C];
+};
+constexpr int64_t kRecBytes = 65536;
+static_assert(sizeof(KdaRec) <= kRecBytes && sizeof(KdaRec) % 16 == 0, "workspace record");
+constexpr int kRecPieces = (int)(sizeof(KdaRec) / 16);  // 16-byte pieces in use
+
+// R and J of block b of the -A record (b = R (R - 1) / 2 + J)
+__device__ __forceinline__ void an_block(int b, int& R, int& J) {
+  R = b < 1 ? 1 : (b < 3 ? 2 : 3);
+  J = b - R * (R - 1) / 2;
+}
+
+// A and P tiles (with the four diagonal inverses) of one chunk over the 8 wavefronts.
+using PrepW0 = Jobs<job(0, 0, 0), job(0, 1, 0), job(0, 2, 0), kNone, kNone>;
+using PrepW1 = Jobs<job(0, 1, 1), job(0, 2, 1), job(0, 3, 0), kNone, kNone>;
+using PrepW2 = Jobs<job(0, 2, 2), job(0, 3, 1), job(1, 0, 0), kNone, kNone>;
+using PrepW3 = Jobs<job(0, 3, 3), job(0, 3, 2), job(1, 1, 0), kNone, kNone>;
+using PrepW4 = Jobs<job(1, 1, 1), job(1, 2, 0), job(1, 2, 1), kNone, kNone>;
+using PrepW5 = Jobs<job(1, 2, 2), job(1, 3, 0), kNone, kNone, kNone>;
+using PrepW6 = Jobs<job(1, 3, 1), job(1, 3, 2), kNone, kNone, kNone>;
+using PrepW7 = Jobs<job(1, 3, 3), kNone, kNone, kNone, kNone>;
+
+// One workgroup per (stream, chunk): stage it as the single kernel does, form the A and P
+// tiles, and write the record.
+__global__ __launch_bounds__(NTH, 1) void kda_prep_kernel(ChunkArgs p, uint8_t* ws, int64_t nchunks) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int l = tid & 63;
+  const int64_t rec = blockIdx.x, bh = rec / nchunks, ci = rec % nchunks;
+  const Streams sr = make_streams(p, bh, tid >= 256);
+  Stage st;
+  stage_load(st, sr, ci * C, tid, 0);
+  stage_chunk(sm, st, tid, w, l);
+  l = opaque(l);
+  f4 unused[2];
+  switch (w) {
+    case 0: produce<PrepW0>(sm, l, unused); break;
+    case 1: produce<PrepW1>(sm, l, unused); break;
+    case 2: produce<PrepW2>(sm, l, unused); break;
+    case 3: produce<PrepW3>(sm, l, unused); break;
+    case 4: produce<PrepW4>(sm, l, unused); break;
+    case 5: produce<PrepW5>(sm, l, unused); break;
+    case 6: produce<PrepW6>(sm, l, unused); break;
+    default: produce<PrepW7>(sm, l, unused); break;
+  }
+  __syncthreads();
+  KdaRec* out = reinterpret_cast<KdaRec*>(ws + rec * kRecBytes);
+  for (int e = tid; e < C * D / 8; e += NTH) {  // the X and output operands carry e^{G_m(R)} already
+    const int r = e >> 4, cc = 8 * (e & 15);
+    const float* em = &sm.tb.em[r >> 4][cc];
+    *reinterpret_cast<h8*>(&out->kl[r][cc]) = scale8(*reinterpret_cast<const h8*>(&sm.kl[r][cc]), em);
+    *reinterpret_cast<h8*>(&out->ql[r][cc]) = scale8(*reinterpret_cast<const h8*>(&sm.ql[r][cc]), em);
+  }
+  for (int e = tid; e < D * C / 8; e += NTH) {
+    const int dk = e >> 3, pc = e & 7;
+    *reinterpret_cast<v4u*>(&out->kt[dk][8 * pc]) = *reinterpret_cast<const v4u*>(&sm.kt[dk][kt_col(dk, 8 * pc)]);
+  }
+  for (int e = tid; e < C * C / 8; e += NTH) {
+    const int r = e >> 3, pc = e & 7;  // columns 8 pc.. lie in block pc / 2
+    v4u x = {0u, 0u, 0u, 0u};
+    if ((pc >> 1) <= (r >> 4)) x = *reinterpret_cast<const v4u*>(&sm.pr.p[r][8 * pc]);
+    *reinterpret_cast<v4u*>(&out->p[r][8 * pc]) = x;
+  }
+  for (int e = tid; e < 6 * 16 * 2; e += NTH) {
+    const int b = e >> 5, rr = (e >> 1) & 15, hh = e & 1;
+    int R, J;
+    an_block(b, R, J);
+    *reinterpret_cast<v4u*>(&out->an[b][rr][8 * hh]) = *reinterpret_cast<const v4u*>(&sm.pr.an[16 * R + rr][16 * J + 8 * hh]);
+  }
+  for (int e = tid; e < 4 * 16 * 2; e += NTH) {
+    const int b = e >> 5, rr = (e >> 1) & 15, hh = e & 1;
+    *reinterpret_cast<v4u*>(&out->td[b][rr][8 * hh]) = *reinterpret_cast<const v4u*>(&sm.pr.td[b][rr][8 * hh]);
+  }
+  for (int e = tid; e < 4 * D; e += NTH) out->em[e / D][e % D] = sm.tb.em[e / D][e % D];
+  if (tid < D) out->gc[tid] = sm.tb.gc[tid];
+  if (tid < C) out->beta[tid] = sm.tb.beta[tid];
+}
+
+// Output tiles only (the A and P tiles come from the record), same owners as in the single
+// kernel.
+using ChainW2 = Jobs<job(2, 0, 0), kNone, kNone, kNone, kNone>;
+using ChainW3 = Jobs<job(2, 0, 1), kNone, kNone, kNone, kNone>;
+using ChainW4 = Jobs<job(2, 1, 0), kNone, kNone, kNone, kNone>;
+using ChainW5 = Jobs<job(2, 1, 1), job(2, 2, 0), kNone, kNone, kNone>;
+using ChainW6 = Jobs<job(2, 2, 1), job(2, 3, 0), kNone, kNone, kNone>;
+using ChainW7 = Jobs<job(2, 3, 1), kNone, kNone, kNone, kNone>;
+
+// Copy of piece e (16 bytes) of a record into its place in LDS.
+__device__ __forceinline__ void put_piece(Smem& sm, int e, v4u x) {
+  if (e < 1024) {
+    *reinterpret_cast<v4u*>(&sm.kl[e >> 4][8 * (e & 15)]) = x;
+  } else if (e < 2048) {
+    e -= 1024;
+    *reinterpret_cast<v4u*>(&sm.ql[e >> 4][8 * (e & 15)]) = x;
+  } else if (e < 3072) {
+    e -= 2048;
+    const int dk = e >> 3;
+    *reinterpret_cast<v4u*>(&sm.kt[dk][kt_col(dk, 8 * (e & 7))]) = x;
+  } else if (e < 3584) {
+    e -= 3072;
+    *reinterpret_cast<v4u*>(&sm.pr.p[e >> 3][8 * (e & 7)]) = x;
+  } else if (e < 3776) {
+    e -= 3584;
+    int R, J;
+    an_block(e >> 5, R, J);
+    *reinterpret_cast<v4u*>(&sm.pr.an[16 * R + ((e >> 1) & 15)][16 * J + 8 * (e & 1)]) = x;
+  } else if (e < 3904) {
+    e -= 3776;
+    *reinterpret_cast<v4u*>(&sm.pr.td[e >> 5][(e >> 1) & 15][8 * (e & 1)]) = x;
+  } else if (e < 4032) {
+    e -= 3904;
+    *reinterpret_cast<v4u*>(&sm.tb.em[e >> 5][4 * (e & 31)]) = x;
+  } else if (e < 4064) {
+    *reinterpret_cast<v4u*>(&sm.tb.gc[4 * (e - 4032)]) = x;
+  } else if (e < kRecPieces) {
+    *reinterpret_cast<v4u*>(&sm.tb.beta[4 * (e - 4064)]) = x;
+  }
+}
+static_assert(kRecPieces == 4080, "record piece map");
+// Pieces tid + NTH i, i = 0..7, of a record: i = 0, 1 fall in kl, 2, 3 in ql, 4, 5 in kt, 6 in
+// p, and 7 in the rest.
+__device__ __forceinline__ void put_record(Smem& sm, int tid, const v4u (&x)[8]) {
+  static_assert(NTH == 512, "piece map assumes 512 threads");
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + NTH * i;
+    *reinterpret_cast<v4u*>(&sm.kl[e >> 4][8 * (e & 15)]) = x[i];
+    *reinterpret_cast<v4u*>(&sm.ql[e >> 4][8 * (e & 15)]) = x[2 + i];
+    const int dk = e >> 3;
+    *reinterpret_cast<v4u*>(&sm.kt[dk][kt_col(dk, 8 * (e & 7))]) = x[4 + i];
+  }
+  *reinterpret_cast<v4u*>(&sm.pr.p[tid >> 3][8 * (tid & 7)]) = x[6];
+  put_piece(sm, tid + NTH * 7, x[7]);
+}
+
+template <typename TOut, bool FROM_WS>
+__global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p, const uint8_t* ws) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -272,135 +548,43 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
 
   const Streams sr = make_streams(p, bh, tid >= 256);
   Stage st;
-  if (nchunks > 0) stage_load(st, sr, 0, tid, c0);
+  // two-kernel form: the record of the next chunk and its value slice, one chunk ahead in
+  // registers (64 KiB per workgroup and chunk: the streaming of the records through each CU's
+  // vector memory path is the larger part of the staging time)
+  const uint8_t* recs = ws + bh * nchunks * kRecBytes;
+  v4u rg[8];
+  auto load_rec = [&](int64_t ci) {
+    const v4u* src = reinterpret_cast<const v4u*>(recs + ci * kRecBytes);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rg[i] = src[tid + NTH * i];  // 4096 pieces of 16 bytes, 4080 used
+    if (tid < 256)
+      st.v = __builtin_amdgcn_raw_buffer_load_b128(sr.v, (int)(((ci * C + (tid >> 2)) * D + c0 + 8 * (tid & 3)) * 2), 0, 0);
+  };
+  if (nchunks > 0) {
+    if constexpr (FROM_WS) load_rec(0);
+    else stage_load(st, sr, 0, tid, c0);
+  }
 
   TOut* O = static_cast<TOut*>(p.o);
-  const int t = tid & 255, g8 = t & 15, rq = t >> 4;
   for (int64_t ci = 0; ci < nchunks; ++ci) {
     const int64_t t0 = ci * C;
     const int n = (int)(T - t0 < C ? T - t0 : C);
     __syncthreads();  // the previous chunk is done with every buffer
 
-    // ---- stage 1: per-channel prefix of log alpha over each group of 4 tokens
-    float gl[4][8];
-    if (tid < 256) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float a = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a += bf_at(st.g[i], e);
-          gl[i][e] = a;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<f4*>(&sm.pf.tot[rq][8 * g8 + 4 * h]) = f4{gl[3][4 * h], gl[3][4 * h + 1], gl[3][4 * h + 2], gl[3][4 * h + 3]};
+    if constexpr (FROM_WS) {
+      put_record(sm, tid, rg);
+      if (tid < 256) *reinterpret_cast<h8*>(&sm.v[tid >> 2][8 * (tid & 3)]) = bf8_to_h8(st.v);
+      if (ci + 1 < nchunks) load_rec(ci + 1);
+      __syncthreads();
+    } else {
+      stage_chunk(sm, st, tid, w, l);
+      if (ci + 1 < nchunks) stage_load(st, sr, t0 + C, tid, c0);
     }
-    __syncthreads();
-
-    // ---- stage 2a: exclusive prefix of the 16 group sums, two channels per lane of wave 4
-    if (w == 4) {
-      typedef float f2 __attribute__((ext_vector_type(2)));
-      f2 x[16], run = {0.f, 0.f};
-#pragma unroll
-      for (int qg = 0; qg < 16; ++qg) x[qg] = *reinterpret_cast<const f2*>(&sm.pf.tot[qg][2 * l]);
-#pragma unroll
-      for (int qg = 0; qg < 16; ++qg) {
-        *reinterpret_cast<f2*>(&sm.pf.tot[qg][2 * l]) = run;
-        run += x[qg];
-      }
-    }
-    __syncthreads();
-
-    // ---- stage 2b: add the sums of the earlier groups; publish G
-    if (tid < 256) {
-      const f4 o0 = *reinterpret_cast<const f4*>(&sm.pf.tot[rq][8 * g8]);
-      const f4 o1 = *reinterpret_cast<const f4*>(&sm.pf.tot[rq][8 * g8 + 4]);
-      const float off[8] = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gl[i][e] += off[e];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          *reinterpret_cast<f4*>(&sm.pf.G[4 * rq + i][8 * g8 + 4 * h]) =
-              f4{gl[i][4 * h], gl[i][4 * h + 1], gl[i][4 * h + 2], gl[i][4 * h + 3]};
-      }
-    }
-    __syncthreads();
-
-    // ---- stage 3: scaled operand tiles, tables, values, beta
-    {
-      const int R = rq >> 2;  // block of this thread's 4 tokens
-      const float* Gm = &sm.pf.G[16 * R + 7][8 * g8];
-      if (tid < 256) {
-        const float* Ge = &sm.pf.G[16 * R + 15][8 * g8];
-        const float* Gl = &sm.pf.G[C - 1][8 * g8];
-        // per channel: e^{G_end - G_m} and e^{G_63 - G_end} (both <= 1); per element one
-        // exponential and one reciprocal: e^{G_end - G_r} = e^{G_end - G_m} / e^{G_r - G_m}
-        float cem[8], c63[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          cem[e] = __expf(fminf(Ge[e] - Gm[e], 0.f));
-          c63[e] = __expf(fminf(Gl[e] - Ge[e], 0.f));
-        }
-        h8 klh[4], kdh[4], krh[4], kth[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float k = bf_at(st.x[i], e);
-            const float el = __expf(gl[i][e] - Gm[e]);          // e^{G_r - G_m}
-            const float ie = __builtin_amdgcn_rcpf(el);          // e^{G_m - G_r}
-            const float er = fminf(cem[e] * ie, 1.f);            // e^{G_end - G_r} <= 1
-            klh[i][e] = (_Float16)(k * el);
-            kdh[i][e] = (_Float16)(k * ie);
-            krh[i][e] = (_Float16)(k * er);
-            kth[i][e] = (_Float16)(k * er * c63[e]);              // e^{G_63 - G_r}
-          }
-          const int row = 4 * rq + i;
-          *reinterpret_cast<h8*>(&sm.kl[row][8 * g8]) = klh[i];
-          *reinterpret_cast<h8*>(&sm.kd[row][8 * g8]) = kdh[i];
-          *reinterpret_cast<h8*>(&sm.kr[row][8 * g8]) = krh[i];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          h4 col;
-          col[0] = kth[0][e]; col[1] = kth[1][e]; col[2] = kth[2][e]; col[3] = kth[3][e];
-          *reinterpret_cast<h4*>(&sm.kt[8 * g8 + e][kt_col(8 * g8 + e, 4 * rq)]) = col;
-        }
-        *reinterpret_cast<h8*>(&sm.v[t >> 2][8 * (t & 3)]) = bf8_to_h8(st.v);
-        if (tid < C) sm.tb.beta[tid] = __uint_as_float(static_cast<uint32_t>(st.beta) << 16);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float* Gr = &sm.pf.G[4 * rq + i][8 * g8];
-          h8 qh;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qh[e] = (_Float16)(bf_at(st.x[i], e) * __expf(Gr[e] - Gm[e]));
-          *reinterpret_cast<h8*>(&sm.ql[4 * rq + i][8 * g8]) = qh;
-        }
-        if (tid >= 384) {  // tables, one channel per thread
-          const int ch = tid - 384;
-#pragma unroll
-          for (int R2 = 0; R2 < 4; ++R2) {
-            const float gm = sm.pf.G[16 * R2 + 7][ch];
-            sm.tb.em[R2][ch] = __expf(gm);
-#pragma unroll
-            for (int J2 = 0; J2 < R2; ++J2) sm.tb.fm[R2][J2][ch] = __expf(fminf(gm - sm.pf.G[16 * J2 + 15][ch], 0.f));
-          }
-          sm.tb.gc[ch] = __expf(sm.pf.G[C - 1][ch]);
-        }
-      }
-    }
-    __syncthreads();
-    if (ci + 1 < nchunks) stage_load(st, sr, t0 + C, tid, c0);
 
     // ---- phase 1: X (waves 0,1), A / P / inverses / O (waves 2..7)
     l = opaque(l);
     int lr = l & 15, lg = l >> 4;
-    if (w == 7) {  // zero the upper P blocks that the O += P U step reads: (0,1) and (2,3)
+    if (!FROM_WS && w == 7) {  // zero the upper P blocks that the O += P U step reads: (0,1) and (2,3)
       for (int e = l; e < 2 * 16 * 16; e += 64) {
         const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
         sm.pr.p[32 * blk + rr][32 * blk + 16 + cc] = (_Float16)0.f;
@@ -417,7 +601,9 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
         const int ch = 32 * kk + 8 * lg;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          X[i] = mfma32(scale8(frag8(&sm.kl[0][0], LQ, 16 * i, 32 * kk, l), &sm.tb.em[i][ch]), sb, X[i]);
+          X[i] = mfma32(FROM_WS ? frag8(&sm.kl[0][0], LQ, 16 * i, 32 * kk, l)
+                                : scale8(frag8(&sm.kl[0][0], LQ, 16 * i, 32 * kk, l), &sm.tb.em[i][ch]),
+                        sb, X[i]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -427,13 +613,24 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
         for (int e = 0; e < 4; ++e) X[i][e] = be[e] * ((float)sm.v[c + e][dv] - X[i][e]);
       }
     } else {
-      switch (w) {
-        case 2: produce<JobsW2>(sm, l, Oacc); break;
-        case 3: produce<JobsW3>(sm, l, Oacc); break;
-        case 4: produce<JobsW4>(sm, l, Oacc); break;
-        case 5: produce<JobsW5>(sm, l, Oacc); break;
-        case 6: produce<JobsW6>(sm, l, Oacc); break;
-        default: produce<JobsW7>(sm, l, Oacc); break;
+      if constexpr (FROM_WS) {
+        switch (w) {
+          case 2: produce<ChainW2, true>(sm, l, Oacc); break;
+          case 3: produce<ChainW3, true>(sm, l, Oacc); break;
+          case 4: produce<ChainW4, true>(sm, l, Oacc); break;
+          case 5: produce<ChainW5, true>(sm, l, Oacc); break;
+          case 6: produce<ChainW6, true>(sm, l, Oacc); break;
+          default: produce<ChainW7, true>(sm, l, Oacc); break;
+        }
+      } else {
+        switch (w) {
+          case 2: produce<JobsW2>(sm, l, Oacc); break;
+          case 3: produce<JobsW3>(sm, l, Oacc); break;
+          case 4: produce<JobsW4>(sm, l, Oacc); break;
+          case 5: produce<JobsW5>(sm, l, Oacc); break;
+          case 6: produce<JobsW6>(sm, l, Oacc); break;
+          default: produce<JobsW7>(sm, l, Oacc); break;
+        }
       }
     }
     __syncthreads();
@@ -518,13 +715,33 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
 
 }  // namespace
 
+size_t kda_workspace_bytes(const ChunkArgs& a) {
+  const int64_t nchunks = (a.T + C - 1) / C;
+  return (size_t)(a.B * a.H * nchunks) * (size_t)kRecBytes;
+}
+
 hipError_t launch_kda_mfma(const ChunkArgs& a, hipStream_t s) {
   const int64_t blocks = a.B * a.H * NT;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (a.out_dtype == GDN_BF16)
-    hipLaunchKernelGGL((kda_chunk_mfma_kernel<__hip_bfloat16>), dim3((unsigned)blocks), dim3(NTH), 0, s, a);
-  else
-    hipLaunchKernelGGL((kda_chunk_mfma_kernel<float>), dim3((unsigned)blocks), dim3(NTH), 0, s, a);
+  const int64_t nchunks = (a.T + C - 1) / C;
+  const size_t need = kda_workspace_bytes(a);
+  const bool two = a.workspace && need > 0 && a.workspace_bytes >= need;
+  const uint8_t* ws = static_cast<const uint8_t*>(a.workspace);
+  if (two) {
+    const int64_t recs = a.B * a.H * nchunks;
+    if (recs > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)recs), dim3(NTH), 0, s, a, static_cast<uint8_t*>(a.workspace),
+                       nchunks);
+    if (a.out_dtype == GDN_BF16)
+      hipLaunchKernelGGL((kda_chunk_mfma_kernel<__hip_bfloat16, true>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
+    else
+      hipLaunchKernelGGL((kda_chunk_mfma_kernel<float, true>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
+  } else {
+    if (a.out_dtype == GDN_BF16)
+      hipLaunchKernelGGL((kda_chunk_mfma_kernel<__hip_bfloat16, false>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
+    else
+      hipLaunchKernelGGL((kda_chunk_mfma_kernel<float, false>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
+  }
   return hipGetLastError();
 }
 

@@ -99,6 +99,10 @@ def test_chunk_validation_errors(g, kda):
 
 def test_workspace_size(g):
     assert g.gdn_chunk_workspace_size(4, 16, 4096, 128) == 0
+    # the matrix-core KDA prefill's two-kernel form: one 64 KiB record per (stream, chunk)
+    assert g.gdn_chunk_workspace_size(2, 32, 8192, 128, kda=True) == 2 * 32 * 128 * 65536
+    assert g.gdn_chunk_workspace_size(1, 3, 65, 128, kda=True) == 3 * 2 * 65536
+    assert g.gdn_chunk_workspace_size(1, 2, 64, 16, chunk=16, in_dtype=__import__("torch").float32, kda=True) == 0
     assert g.gdn_chunk_workspace_size(1, 2, 64, 16, chunk=16, in_dtype=__import__("torch").float32) == 0
     with pytest.raises(g.GdnError):
         g.gdn_chunk_workspace_size(1, 1, 64, 96)

@@ -193,6 +193,29 @@ def test_kda_mfma_snapshots_resume_empty():
     assert o.shape == (1, 2, 0, 128) and torch.equal(sf.cpu(), e["s0"])
 
 
+@pytest.mark.parametrize("T,every", [(200, 0), (256, 64), (1, 0)])
+def test_kda_two_kernel_form_is_the_single_kernel(T, every):
+    """With its workspace the KDA prefill computes every chunk's state-independent tiles in a
+    separate parallel kernel; the sequential kernel then runs the same arithmetic on the same
+    operands, so outputs, final state and snapshots equal the single kernel's bit for bit."""
+    import gated_deltanet_state_amd as g
+    say(f"kda two-kernel form T={T} every={every}")
+    inp = synth.make_prefill(2, 3, T, 128, 128, torch.bfloat16, kda=True, s0_std=0.01, seed=70 + T)
+    d = {k: v.cuda() for k, v in inp.items()}
+    need = g.gdn_chunk_workspace_size(2, 3, T, 128, kda=True, ckpt_every=every)
+    assert need == 2 * 3 * ((T + 63) // 64) * 65536
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")   # stale bytes must not matter
+    run = lambda w: g.kda_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["s0"], ckpt_every=every,
+                                    out_dtype=torch.float32, workspace=w)
+    a, b = run(False), run(ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    if every:
+        assert torch.equal(a[2], b[2])
+    with pytest.raises(g.GdnError):   # a workspace that is too small is refused
+        run(ws[:need - 16])
+
+
 def test_workload_kda_full_size_sampled_heads():
     """B=2, H=32, T=8192, d=128, chunk 64, bf16, per-channel gates: the oracle follows 3
     sampled (batch, head) streams through the whole sequence."""
