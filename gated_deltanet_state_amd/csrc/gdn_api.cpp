@@ -156,7 +156,16 @@ gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, con
                       overlaps(a.workspace, a.workspace_bytes, s0, s0 ? state_bytes : 0) ||
                       overlaps(a.workspace, a.workspace_bytes, s_ckpt, s_ckpt ? ck_bytes : 0)))
     return GDN_ERROR_INVALID_VALUE;
-  (void)in_elem;
+  if (a.workspace) {  // the preparation kernel writes the workspace while it reads the inputs
+    const size_t tok = (size_t)BH * (size_t)a.T;
+    const size_t qkv_bytes = tok * (size_t)a.D * in_elem;
+    const size_t la_bytes = tok * (is_kda ? (size_t)a.D : 1) * in_elem;
+    if (overlaps(a.workspace, a.workspace_bytes, q, qkv_bytes) || overlaps(a.workspace, a.workspace_bytes, k, qkv_bytes) ||
+        overlaps(a.workspace, a.workspace_bytes, v, qkv_bytes) ||
+        overlaps(a.workspace, a.workspace_bytes, beta, tok * in_elem) ||
+        overlaps(a.workspace, a.workspace_bytes, log_alpha, la_bytes))
+      return GDN_ERROR_INVALID_VALUE;
+  }
 
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
   a.s0 = s0; a.o = o; a.s_final = s_final; a.s_ckpt = s_ckpt;

@@ -97,6 +97,33 @@ def test_chunk_validation_errors(g, kda):
     assert _call(g, _desc(g, B=0), kda) == g.GDN_SUCCESS
 
 
+def test_kda_workspace_validation(g):
+    """The matrix-core KDA prefill's workspace: too small, misaligned, or overlapping an input or
+    an output is INVALID_VALUE before anything is launched (B=1, H=2, T=64: two records of
+    64 KiB)."""
+    INV = g.GDN_ERROR_INVALID_VALUE
+    d = _desc(g)
+    need = g.gdn_chunk_workspace_size(1, 2, 64, 128, kda=True)
+    assert need == 2 * 65536
+    ws = FAKE + 0x40000000
+    call = lambda addr, nbytes, **kw: _call_ws(g, d, addr, nbytes, **kw)
+    assert call(ws, need - 16) == INV                 # too small
+    assert call(ws + 8, need) == INV                  # misaligned
+    assert call(FAKE + 0x6000000 - 64, need) == INV   # runs into o
+    assert call(FAKE - 0x100, need) == INV            # covers q
+    assert call(FAKE + 0x3000000, need) == INV        # covers beta and beyond
+
+
+def _call_ws(g, d, ws, nbytes, **ptrs):
+    p = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, beta=FAKE + 0x3000000,
+             log_alpha=FAKE + 0x4000000, s0=FAKE + 0x5000000, o=FAKE + 0x6000000,
+             s_final=FAKE + 0x7000000, s_ckpt=FAKE + 0x8000000)
+    p.update(ptrs)
+    args = [ctypes.c_void_p(p[n]) if p[n] is not None else None
+            for n in ("q", "k", "v", "beta", "log_alpha", "s0", "o", "s_final", "s_ckpt")]
+    return g.lib.kda_chunk_fwd(ctypes.byref(d), *args, ctypes.c_void_p(ws), nbytes, None)
+
+
 def test_workspace_size(g):
     assert g.gdn_chunk_workspace_size(4, 16, 4096, 128) == 0
     # the matrix-core KDA prefill's two-kernel form: one 64 KiB record per (stream, chunk)
