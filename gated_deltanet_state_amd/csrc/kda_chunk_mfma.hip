@@ -403,17 +403,13 @@ using PrepW5 = Jobs<job(1, 2, 2), job(1, 3, 0), kNone, kNone, kNone>;
 using PrepW6 = Jobs<job(1, 3, 1), job(1, 3, 2), kNone, kNone, kNone>;
 using PrepW7 = Jobs<job(1, 3, 3), kNone, kNone, kNone, kNone>;
 
-// One workgroup per (stream, chunk): stage it as the single kernel does, form the A and P
-// tiles, and write the record.
-__global__ __launch_bounds__(NTH, 1) void kda_prep_kernel(ChunkArgs p, uint8_t* ws, int64_t nchunks) {
-  __shared__ Smem sm;
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int l = tid & 63;
-  const int64_t rec = blockIdx.x, bh = rec / nchunks, ci = rec % nchunks;
-  const Streams sr = make_streams(p, bh, tid >= 256);
-  Stage st;
-  stage_load(st, sr, ci * C, tid, 0);
+// Records are spread over a grid of at most one workgroup per CU (the LDS holds one); each
+// workgroup walks its records in order, staging each one as the single kernel does, forming the
+// A and P tiles and writing the record.  The inputs of the next record are loaded while the
+// current one is computed (two register sets), and the record writes are never waited for, so
+// neither latency reaches the workgroup's critical path.
+__device__ __forceinline__ void prep_record(Smem& sm, const Stage& st, uint8_t* ws, int64_t rec, int tid, int w,
+                                            int l) {
   stage_chunk(sm, st, tid, w, l);
   l = opaque(l);
   f4 unused[2];
@@ -458,6 +454,33 @@ __global__ __launch_bounds__(NTH, 1) void kda_prep_kernel(ChunkArgs p, uint8_t* 
   for (int e = tid; e < 4 * D; e += NTH) out->em[e / D][e % D] = sm.tb.em[e / D][e % D];
   if (tid < D) out->gc[tid] = sm.tb.gc[tid];
   if (tid < C) out->beta[tid] = sm.tb.beta[tid];
+  // before its first barrier the next record's staging writes only the group sums, which share
+  // no bytes with the tiles read above; everything else it writes comes after that barrier
+}
+static_assert(offsetof(Prefix, tot) >= offsetof(Products, nt), "group sums overlap the record tiles");
+
+__global__ __launch_bounds__(NTH, 1) void kda_prep_kernel(ChunkArgs p, uint8_t* ws, int64_t nchunks) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int64_t nrec = p.B * p.H * nchunks, step = gridDim.x;
+  auto load = [&](int64_t rec, Stage& st) {
+    if (rec >= nrec) return;
+    const int64_t bh = rec / nchunks, ci = rec % nchunks;
+    stage_load(st, make_streams(p, bh, tid >= 256), ci * C, tid, 0);
+  };
+  Stage sa, sb;
+  int64_t rec = blockIdx.x;
+  load(rec, sa);
+  load(rec + step, sb);
+  for (; rec < nrec; rec += 2 * step) {  // the bounds are uniform over the workgroup
+    prep_record(sm, sa, ws, rec, tid, w, l);
+    load(rec + 2 * step, sa);
+    if (rec + step >= nrec) break;
+    prep_record(sm, sb, ws, rec + step, tid, w, l);
+    load(rec + 3 * step, sb);
+  }
 }
 
 // Output tiles only (the A and P tiles come from the record), same owners as in the single
@@ -730,7 +753,9 @@ hipError_t launch_kda_mfma(const ChunkArgs& a, hipStream_t s) {
   if (two) {
     const int64_t recs = a.B * a.H * nchunks;
     if (recs > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)recs), dim3(NTH), 0, s, a, static_cast<uint8_t*>(a.workspace),
+    // one workgroup per CU, each walking every 256th record
+    const int64_t grid = recs < 256 ? recs : 256;
+    hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)grid), dim3(NTH), 0, s, a, static_cast<uint8_t*>(a.workspace),
                        nchunks);
     if (a.out_dtype == GDN_BF16)
       hipLaunchKernelGGL((kda_chunk_mfma_kernel<__hip_bfloat16, true>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
