@@ -23,6 +23,10 @@
 // 8 wavefronts), without its cross-chunk pipelining: the per-channel operand tiles fill the
 // LDS.  Per chunk: stage (log-gate prefix per channel, scaled operand tiles) | Gram/score
 // tiles, diagonal inverses, X, O | substitution | O += P U and the state hand-off.
+// Two-kernel form (when the caller passes a workspace): a preparation kernel writes each chunk's
+// state-independent operands once per stream as a record, and a sequential kernel streams the
+// records through LDS (double-buffered, LDS-direct copies) instead of the four value-slice
+// workgroups each staging and multiplying them.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
@@ -167,7 +171,7 @@ struct Jobs {
 };
 
 // Gram / score tile (M = j, N = r): the lane holds r = 16 R + lr, j = 16 J + 4 lg + i.
-template <class L, bool PRESCALED = false>
+template <class L>
 __device__ __forceinline__ void produce(Smem& sm, int l, f4* Oacc) {
   const int lr = l & 15, lg = l >> 4;
   f4 acc[5];
@@ -183,7 +187,7 @@ __device__ __forceinline__ void produce(Smem& sm, int l, f4* Oacc) {
       const int kind = jb >> 4, R = (jb >> 2) & 3, J = jb & 3;
       if (kind == 2) {  // O^T[dv][c] += sum S[dv][ch] (Q Gamma)[c][ch]: B operand = ql rows c * e^{G_m(R)}
         const h8 qf = frag8(&sm.ql[0][0], LQ, 16 * R, 32 * kk, l);
-        const h8 qb = PRESCALED ? qf : scale8(qf, &sm.tb.em[R][ch]);
+        const h8 qb = scale8(qf, &sm.tb.em[R][ch]);
         acc[t] = mfma32(frag8(&sm.s[0][0], LQ, 16 * J, 32 * kk, l), qb, acc[t]);
       } else {
         const _Float16* Am = (R == J) ? &sm.kd[0][0] : &sm.kr[0][0];
@@ -372,20 +376,42 @@ __device__ __forceinline__ void stage_chunk(Smem& sm, const Stage& st, int tid, 
 // runs X, the substitution, the outputs and the state hand-off.  The single kernel recomputes
 // that state-independent work in each of the NT workgroups of a stream, one chunk after
 // another.  Both forms run the same arithmetic on the same operands.
-struct KdaRec {
+// The record is the LDS image the sequential kernel computes from.  Its fp16 tiles store the
+// 16-byte chunk c of row r at chunk c ^ swz128(r) (128-wide rows) or c ^ swz64(r) (64-wide
+// rows).  A fragment read (lanes on 16 consecutive rows, two adjacent chunks per 32 lanes) and a
+// row-major 16-byte copy (two rows of all chunks per 32 lanes) then touch every LDS bank once.
+__device__ __forceinline__ int swz128(int r) { return ((r >> 1) & 7) << 1; }
+__device__ __forceinline__ int swz64(int r) { return ((r >> 2) & 3) << 1; }
+template <int W>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(W == D || W == C, "tile width");
+  return W == D ? swz128(r) : swz64(r);
+}
+// Element (r, col) of a swizzled W-wide tile.
+template <int W, typename T>
+__device__ __forceinline__ T* sat(T* base, int r, int col) {
+  return base + r * W + 8 * ((col >> 3) ^ swz<W>(r)) + (col & 7);
+}
+// Operand fragment of a swizzled W-wide tile: rows m0 + l%16, columns k0 + 8 (l/16) .. +7.
+template <int W>
+__device__ __forceinline__ h8 sfrag8(const _Float16* base, int m0, int k0, int lane) {
+  return *reinterpret_cast<const h8*>(sat<W>(base, m0 + (lane & 15), k0 + 8 * (lane >> 4)));
+}
+
+struct alignas(16) KdaRec {
   _Float16 kl[C][D];       // k_r e^{G_r - G_m(R)} e^{G_m(R)}, rounded as the single kernel rounds it at use
   _Float16 ql[C][D];       // q_r e^{G_r - G_m(R)} e^{G_m(R)}, likewise
   _Float16 kt[D][C];       // k_c e^{G_63 - G_c}, [d_k][token]
   _Float16 p[C][C];        // tril((Q*Gamma)(K/Gamma)^T), zero above the diagonal blocks
-  _Float16 an[6][16][16];  // -A, blocks (R, J), R > J, in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+  _Float16 an[6][16][16];  // -A, blocks (R, J), R > J, at R (R - 1) / 2 + J
   _Float16 td[4][16][16];  // inverses of the diagonal blocks of (I + A), row-major
-  float em[4][D];          // e^{G_m(R)}
   float gc[D];             // e^{G_63}
   float beta[C];
+  uint8_t pad[256];        // whole KiB: the copy into LDS moves 1 KiB per wavefront instruction
 };
-constexpr int64_t kRecBytes = 65536;
-static_assert(sizeof(KdaRec) <= kRecBytes && sizeof(KdaRec) % 16 == 0, "workspace record");
-constexpr int kRecPieces = (int)(sizeof(KdaRec) / 16);  // 16-byte pieces in use
+constexpr int64_t kRecBytes = 65536;  // record stride in the workspace
+constexpr int kRecKiB = (int)(sizeof(KdaRec) / 1024);
+static_assert(sizeof(KdaRec) == 62 * 1024 && sizeof(KdaRec) <= kRecBytes, "workspace record");
 
 // R and J of block b of the -A record (b = R (R - 1) / 2 + J)
 __device__ __forceinline__ void an_block(int b, int& R, int& J) {
@@ -428,18 +454,18 @@ __device__ __forceinline__ void prep_record(Smem& sm, const Stage& st, uint8_t* 
   for (int e = tid; e < C * D / 8; e += NTH) {  // the X and output operands carry e^{G_m(R)} already
     const int r = e >> 4, cc = 8 * (e & 15);
     const float* em = &sm.tb.em[r >> 4][cc];
-    *reinterpret_cast<h8*>(&out->kl[r][cc]) = scale8(*reinterpret_cast<const h8*>(&sm.kl[r][cc]), em);
-    *reinterpret_cast<h8*>(&out->ql[r][cc]) = scale8(*reinterpret_cast<const h8*>(&sm.ql[r][cc]), em);
+    *reinterpret_cast<h8*>(sat<D>(&out->kl[0][0], r, cc)) = scale8(*reinterpret_cast<const h8*>(&sm.kl[r][cc]), em);
+    *reinterpret_cast<h8*>(sat<D>(&out->ql[0][0], r, cc)) = scale8(*reinterpret_cast<const h8*>(&sm.ql[r][cc]), em);
   }
   for (int e = tid; e < D * C / 8; e += NTH) {
     const int dk = e >> 3, pc = e & 7;
-    *reinterpret_cast<v4u*>(&out->kt[dk][8 * pc]) = *reinterpret_cast<const v4u*>(&sm.kt[dk][kt_col(dk, 8 * pc)]);
+    *reinterpret_cast<v4u*>(sat<C>(&out->kt[0][0], dk, 8 * pc)) = *reinterpret_cast<const v4u*>(&sm.kt[dk][kt_col(dk, 8 * pc)]);
   }
   for (int e = tid; e < C * C / 8; e += NTH) {
     const int r = e >> 3, pc = e & 7;  // columns 8 pc.. lie in block pc / 2
     v4u x = {0u, 0u, 0u, 0u};
     if ((pc >> 1) <= (r >> 4)) x = *reinterpret_cast<const v4u*>(&sm.pr.p[r][8 * pc]);
-    *reinterpret_cast<v4u*>(&out->p[r][8 * pc]) = x;
+    *reinterpret_cast<v4u*>(sat<C>(&out->p[0][0], r, 8 * pc)) = x;
   }
   for (int e = tid; e < 6 * 16 * 2; e += NTH) {
     const int b = e >> 5, rr = (e >> 1) & 15, hh = e & 1;
@@ -451,7 +477,6 @@ __device__ __forceinline__ void prep_record(Smem& sm, const Stage& st, uint8_t* 
     const int b = e >> 5, rr = (e >> 1) & 15, hh = e & 1;
     *reinterpret_cast<v4u*>(&out->td[b][rr][8 * hh]) = *reinterpret_cast<const v4u*>(&sm.pr.td[b][rr][8 * hh]);
   }
-  for (int e = tid; e < 4 * D; e += NTH) out->em[e / D][e % D] = sm.tb.em[e / D][e % D];
   if (tid < D) out->gc[tid] = sm.tb.gc[tid];
   if (tid < C) out->beta[tid] = sm.tb.beta[tid];
   // before its first barrier the next record's staging writes only the group sums, which share
@@ -485,63 +510,8 @@ __global__ __launch_bounds__(NTH, 1) void kda_prep_kernel(ChunkArgs p, uint8_t* 
 
 // Output tiles only (the A and P tiles come from the record), same owners as in the single
 // kernel.
-using ChainW2 = Jobs<job(2, 0, 0), kNone, kNone, kNone, kNone>;
-using ChainW3 = Jobs<job(2, 0, 1), kNone, kNone, kNone, kNone>;
-using ChainW4 = Jobs<job(2, 1, 0), kNone, kNone, kNone, kNone>;
-using ChainW5 = Jobs<job(2, 1, 1), job(2, 2, 0), kNone, kNone, kNone>;
-using ChainW6 = Jobs<job(2, 2, 1), job(2, 3, 0), kNone, kNone, kNone>;
-using ChainW7 = Jobs<job(2, 3, 1), kNone, kNone, kNone, kNone>;
-
-// Copy of piece e (16 bytes) of a record into its place in LDS.
-__device__ __forceinline__ void put_piece(Smem& sm, int e, v4u x) {
-  if (e < 1024) {
-    *reinterpret_cast<v4u*>(&sm.kl[e >> 4][8 * (e & 15)]) = x;
-  } else if (e < 2048) {
-    e -= 1024;
-    *reinterpret_cast<v4u*>(&sm.ql[e >> 4][8 * (e & 15)]) = x;
-  } else if (e < 3072) {
-    e -= 2048;
-    const int dk = e >> 3;
-    *reinterpret_cast<v4u*>(&sm.kt[dk][kt_col(dk, 8 * (e & 7))]) = x;
-  } else if (e < 3584) {
-    e -= 3072;
-    *reinterpret_cast<v4u*>(&sm.pr.p[e >> 3][8 * (e & 7)]) = x;
-  } else if (e < 3776) {
-    e -= 3584;
-    int R, J;
-    an_block(e >> 5, R, J);
-    *reinterpret_cast<v4u*>(&sm.pr.an[16 * R + ((e >> 1) & 15)][16 * J + 8 * (e & 1)]) = x;
-  } else if (e < 3904) {
-    e -= 3776;
-    *reinterpret_cast<v4u*>(&sm.pr.td[e >> 5][(e >> 1) & 15][8 * (e & 1)]) = x;
-  } else if (e < 4032) {
-    e -= 3904;
-    *reinterpret_cast<v4u*>(&sm.tb.em[e >> 5][4 * (e & 31)]) = x;
-  } else if (e < 4064) {
-    *reinterpret_cast<v4u*>(&sm.tb.gc[4 * (e - 4032)]) = x;
-  } else if (e < kRecPieces) {
-    *reinterpret_cast<v4u*>(&sm.tb.beta[4 * (e - 4064)]) = x;
-  }
-}
-static_assert(kRecPieces == 4080, "record piece map");
-// Pieces tid + NTH i, i = 0..7, of a record: i = 0, 1 fall in kl, 2, 3 in ql, 4, 5 in kt, 6 in
-// p, and 7 in the rest.
-__device__ __forceinline__ void put_record(Smem& sm, int tid, const v4u (&x)[8]) {
-  static_assert(NTH == 512, "piece map assumes 512 threads");
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int e = tid + NTH * i;
-    *reinterpret_cast<v4u*>(&sm.kl[e >> 4][8 * (e & 15)]) = x[i];
-    *reinterpret_cast<v4u*>(&sm.ql[e >> 4][8 * (e & 15)]) = x[2 + i];
-    const int dk = e >> 3;
-    *reinterpret_cast<v4u*>(&sm.kt[dk][kt_col(dk, 8 * (e & 7))]) = x[4 + i];
-  }
-  *reinterpret_cast<v4u*>(&sm.pr.p[tid >> 3][8 * (tid & 7)]) = x[6];
-  put_piece(sm, tid + NTH * 7, x[7]);
-}
-
-template <typename TOut, bool FROM_WS>
-__global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p, const uint8_t* ws) {
+template <typename TOut>
+__global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -571,22 +541,7 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p, con
 
   const Streams sr = make_streams(p, bh, tid >= 256);
   Stage st;
-  // two-kernel form: the record of the next chunk and its value slice, one chunk ahead in
-  // registers (64 KiB per workgroup and chunk: the streaming of the records through each CU's
-  // vector memory path is the larger part of the staging time)
-  const uint8_t* recs = ws + bh * nchunks * kRecBytes;
-  v4u rg[8];
-  auto load_rec = [&](int64_t ci) {
-    const v4u* src = reinterpret_cast<const v4u*>(recs + ci * kRecBytes);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rg[i] = src[tid + NTH * i];  // 4096 pieces of 16 bytes, 4080 used
-    if (tid < 256)
-      st.v = __builtin_amdgcn_raw_buffer_load_b128(sr.v, (int)(((ci * C + (tid >> 2)) * D + c0 + 8 * (tid & 3)) * 2), 0, 0);
-  };
-  if (nchunks > 0) {
-    if constexpr (FROM_WS) load_rec(0);
-    else stage_load(st, sr, 0, tid, c0);
-  }
+  if (nchunks > 0) stage_load(st, sr, 0, tid, c0);
 
   TOut* O = static_cast<TOut*>(p.o);
   for (int64_t ci = 0; ci < nchunks; ++ci) {
@@ -594,20 +549,13 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p, con
     const int n = (int)(T - t0 < C ? T - t0 : C);
     __syncthreads();  // the previous chunk is done with every buffer
 
-    if constexpr (FROM_WS) {
-      put_record(sm, tid, rg);
-      if (tid < 256) *reinterpret_cast<h8*>(&sm.v[tid >> 2][8 * (tid & 3)]) = bf8_to_h8(st.v);
-      if (ci + 1 < nchunks) load_rec(ci + 1);
-      __syncthreads();
-    } else {
-      stage_chunk(sm, st, tid, w, l);
-      if (ci + 1 < nchunks) stage_load(st, sr, t0 + C, tid, c0);
-    }
+    stage_chunk(sm, st, tid, w, l);
+    if (ci + 1 < nchunks) stage_load(st, sr, t0 + C, tid, c0);
 
     // ---- phase 1: X (waves 0,1), A / P / inverses / O (waves 2..7)
     l = opaque(l);
     int lr = l & 15, lg = l >> 4;
-    if (!FROM_WS && w == 7) {  // zero the upper P blocks that the O += P U step reads: (0,1) and (2,3)
+    if (w == 7) {  // zero the upper P blocks that the O += P U step reads: (0,1) and (2,3)
       for (int e = l; e < 2 * 16 * 16; e += 64) {
         const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
         sm.pr.p[32 * blk + rr][32 * blk + 16 + cc] = (_Float16)0.f;
@@ -624,9 +572,7 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p, con
         const int ch = 32 * kk + 8 * lg;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          X[i] = mfma32(FROM_WS ? frag8(&sm.kl[0][0], LQ, 16 * i, 32 * kk, l)
-                                : scale8(frag8(&sm.kl[0][0], LQ, 16 * i, 32 * kk, l), &sm.tb.em[i][ch]),
-                        sb, X[i]);
+          X[i] = mfma32(scale8(frag8(&sm.kl[0][0], LQ, 16 * i, 32 * kk, l), &sm.tb.em[i][ch]), sb, X[i]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -636,24 +582,13 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p, con
         for (int e = 0; e < 4; ++e) X[i][e] = be[e] * ((float)sm.v[c + e][dv] - X[i][e]);
       }
     } else {
-      if constexpr (FROM_WS) {
-        switch (w) {
-          case 2: produce<ChainW2, true>(sm, l, Oacc); break;
-          case 3: produce<ChainW3, true>(sm, l, Oacc); break;
-          case 4: produce<ChainW4, true>(sm, l, Oacc); break;
-          case 5: produce<ChainW5, true>(sm, l, Oacc); break;
-          case 6: produce<ChainW6, true>(sm, l, Oacc); break;
-          default: produce<ChainW7, true>(sm, l, Oacc); break;
-        }
-      } else {
-        switch (w) {
-          case 2: produce<JobsW2>(sm, l, Oacc); break;
-          case 3: produce<JobsW3>(sm, l, Oacc); break;
-          case 4: produce<JobsW4>(sm, l, Oacc); break;
-          case 5: produce<JobsW5>(sm, l, Oacc); break;
-          case 6: produce<JobsW6>(sm, l, Oacc); break;
-          default: produce<JobsW7>(sm, l, Oacc); break;
-        }
+      switch (w) {
+        case 2: produce<JobsW2>(sm, l, Oacc); break;
+        case 3: produce<JobsW3>(sm, l, Oacc); break;
+        case 4: produce<JobsW4>(sm, l, Oacc); break;
+        case 5: produce<JobsW5>(sm, l, Oacc); break;
+        case 6: produce<JobsW6>(sm, l, Oacc); break;
+        default: produce<JobsW7>(sm, l, Oacc); break;
       }
     }
     __syncthreads();
@@ -736,6 +671,232 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p, con
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Sequential kernel of the two-kernel form.  Per chunk it needs the state-independent operands
+// of the chunk's record and its own state slice: X, the substitution, the outputs and the state
+// hand-off, on the operands the single kernel uses, in the same order (same bits).  The record
+// of chunk c + 1 is copied into the other LDS buffer by LDS-direct loads, issued right after the
+// barrier that opens chunk c, so the copy (bound by the LDS write rate) runs under chunk c's
+// work instead of before it.  The two buffers are separate LDS objects, which tells the
+// compiler that reads of one never wait for the copy into the other.
+struct alignas(16) ChainLocal {
+  alignas(16) _Float16 s[DVT][D];           // fp16 copy of the state slice [d_v][d_k], swizzled (128-wide)
+  alignas(16) _Float16 v[2][C][DVT + 8];    // value slice [token][d_v], by chunk parity
+  alignas(16) _Float16 u[DVT][C];           // U [d_v][token], swizzled (64-wide)
+};
+static_assert(2 * sizeof(KdaRec) + sizeof(ChainLocal) <= 160 * 1024, "LDS budget");
+
+// Barrier between phases of a chunk: the data handed over is written by LDS instructions, so
+// each wave waits for its own LDS operations only.  (A barrier with a workgroup release fence
+// would also wait for the LDS-direct copy of the next record, which has until the next chunk.)
+__device__ __forceinline__ void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Copy of KiB blocks k0, k0 + step, .. below k1 of a record into LDS, one wavefront instruction
+// per block (lane l moves bytes 16 l .. 16 l + 15).  A wave issuing these stalls until the
+// copy path has taken them (about 50 bytes per cycle per CU), so the copy is issued by waves
+// that have nothing else to do at that point.
+__device__ __forceinline__ void fetch_blocks(KdaRec& dst, const uint8_t* src, int k0, int k1, int step, int l) {
+  uint8_t* d = reinterpret_cast<uint8_t*>(&dst);
+  for (int k = k0; k < k1; k += step)
+    __builtin_amdgcn_global_load_lds(src + 1024 * k + 16 * l, (__attribute__((address_space(3))) void*)(d + 1024 * k),
+                                     16, 0, 0);
+}
+// Split of the next record's copy: waves 2..7 take blocks below kSplit during the substitution
+// (which runs on waves 0 and 1 alone); waves 0 and 1 take the rest at the end of the chunk,
+// where they finish earlier than the output waves.
+constexpr int kSplit = 50;
+static_assert(kSplit <= kRecKiB, "copy split");
+
+// One chunk: record rc (already in LDS), values in loc.v[vb].  Issues the copy of the next
+// record into nx.
+template <typename TOut>
+__device__ __forceinline__ void chain_chunk(const KdaRec& rc, KdaRec& nx, ChainLocal& loc, int vb, const ChunkArgs& p,
+                                            const Streams& sr, const uint8_t* recs, int64_t ci, int64_t nchunks,
+                                            int64_t bh, int c0, int tid, int w, int l, f4 (&S)[2], v4u& vv) {
+  const int64_t T = p.T, t0 = ci * C;
+  const int n = (int)(T - t0 < C ? T - t0 : C);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0): this wave's part of the record has landed
+  __syncthreads();  // all parts have; chunk ci - 1 is done with the other buffer and value slot
+  const bool more = ci + 1 < nchunks;
+  const uint8_t* next = recs + (ci + 1) * kRecBytes;
+  if (more && tid < 256)
+    vv = __builtin_amdgcn_raw_buffer_load_b128(sr.v, (int)((((ci + 1) * C + (tid >> 2)) * D + c0 + 8 * (tid & 3)) * 2), 0, 0);
+
+  // ---- phase 1: X (waves 0,1), O = (Q Gamma) S^T tiles (waves 2..7)
+  l = opaque(l);
+  int lr = l & 15, lg = l >> 4;
+  f4 X[4], Oacc[2];
+  if (w < 2) {
+    const int db = w, dv = 16 * db + lr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X[i] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const h8 sb = sfrag8<D>(&loc.s[0][0], 16 * db, 32 * kk, l);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[i] = mfma32(sfrag8<D>(&rc.kl[0][0], 16 * i, 32 * kk, l), sb, X[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * i + 4 * lg;
+      const f4 be = *reinterpret_cast<const f4*>(&rc.beta[c]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) X[i][e] = be[e] * ((float)loc.v[vb][c + e][dv] - X[i][e]);
+    }
+  } else {
+    const int no = o_count(w);
+    f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        if (t2 >= no) continue;
+        int cb, db;
+        o_tile(w, t2, cb, db);
+        acc[t2] = mfma32(sfrag8<D>(&loc.s[0][0], 16 * db, 32 * kk, l), sfrag8<D>(&rc.ql[0][0], 16 * cb, 32 * kk, l),
+                         acc[t2]);
+      }
+    }
+    Oacc[0] = acc[0];
+    Oacc[1] = acc[1];
+  }
+  phase_barrier();
+
+  // ---- phase 2: block forward substitution (waves 0,1); most of the next record's copy (2..7)
+  l = opaque(l);
+  lr = l & 15, lg = l >> 4;
+  // values of the next chunk into the other slot (chunk ci - 1 has read it; read after the next
+  // chunk's opening barrier), before any copy is issued: waiting for them waits for nothing else
+  if (more && tid < 256) *reinterpret_cast<h8*>(&loc.v[vb ^ 1][tid >> 2][8 * (tid & 3)]) = bf8_to_h8(vv);
+  if (w >= 2 && more) fetch_blocks(nx, next, w - 2, kSplit, NTH / 64 - 2, l);
+  if (w < 2) {
+    const int dv = 16 * w + lr;
+    h4 an[6], tdf[4];
+#pragma unroll
+    for (int i = 0, m = 0; i < 4; ++i) {
+      tdf[i] = frag4(&rc.td[i][0][0], 16, 0, 0, l);
+#pragma unroll
+      for (int j = 0; j < i; ++j, ++m) an[m] = frag4(&rc.an[m][0][0], 16, 0, 0, l);
+    }
+    h4 Uh[4];
+#pragma unroll
+    for (int i = 0, m = 0; i < 4; ++i) {
+      f4 acc = X[i];
+#pragma unroll
+      for (int j = 0; j < i; ++j, ++m) acc = mfma16(an[m], Uh[j], acc);
+      Uh[i] = to_h4(mfma16(tdf[i], to_h4(acc), f4{0.f, 0.f, 0.f, 0.f}));
+      *reinterpret_cast<h4*>(sat<C>(&loc.u[0][0], dv, 16 * i + 4 * lg)) = Uh[i];
+    }
+  }
+  phase_barrier();
+
+  // ---- phase 3: O += U^T P^T, output (waves 2..7); S <- S Diag(Gamma_63) + U^T (K e^{G_63 - G})
+  l = opaque(l);
+  lr = l & 15, lg = l >> 4;
+  if (w >= 2) {
+    TOut* O = static_cast<TOut*>(p.o);
+    const int no = o_count(w);
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      if (t2 >= no) continue;
+      int cb, db;
+      o_tile(w, t2, cb, db);
+      f4 acc = Oacc[t2];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        if (kc == 1 && cb < 2) continue;
+        acc = mfma32(sfrag8<C>(&loc.u[0][0], 16 * db, 32 * kc, l), sfrag8<C>(&rc.p[0][0], 16 * cb, 32 * kc, l), acc);
+      }
+      const int c = 16 * cb + lr;
+      if (c < n) store_o4<TOut>(O, (bh * T + t0 + c) * D + c0 + 16 * db + 4 * lg, acc);
+    }
+  }
+  {
+    // The snapshot store goes through a buffer descriptor whose range is empty when no snapshot
+    // is due, so the phase has no branch (a branch here makes the compiler wait for the copy).
+    const bool snap = p.s_ckpt && n == C && ((t0 + n) % p.ckpt_every) == 0;
+    const int64_t idx = snap ? (t0 + n) / p.ckpt_every - 1 : 0;
+    const auto snr = __builtin_amdgcn_make_buffer_rsrc(
+        snap ? (void*)(p.s_ckpt + ((bh * p.n_ckpt + idx) * D + c0) * D) : (void*)p.o, 0, snap ? DVT * D * 4 : 0,
+        kRsrcWord3);
+    const int dk = 16 * w + 4 * lg;
+    const f4 gcv = *reinterpret_cast<const f4*>(&rc.gc[dk]);
+    // every operand is read before the first LDS write of the phase (an LDS read after an LDS
+    // write would make the compiler wait for the copy in flight)
+    h8 ka[2], uf[2][2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      ka[kc] = sfrag8<C>(&rc.kt[0][0], 16 * w, 32 * kc, l);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) uf[db][kc] = sfrag8<C>(&loc.u[0][0], 16 * db, 32 * kc, l);
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      f4 acc = S[db] * gcv;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) acc = mfma32(ka[kc], uf[db][kc], acc);
+      S[db] = acc;
+      const int dv = 16 * db + lr;
+      *reinterpret_cast<h4*>(sat<D>(&loc.s[0][0], dv, dk)) = to_h4(acc);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, acc), snr, (dv * D + dk) * 4, 0, 0);
+    }
+  }
+  if (w < 2 && more) fetch_blocks(nx, next, kSplit + w, kRecKiB, 2, l);
+}
+
+template <typename TOut>
+__global__ __launch_bounds__(NTH, 1) void kda_chain_kernel(ChunkArgs p, const uint8_t* ws) {
+  __shared__ KdaRec rec0;
+  __shared__ KdaRec rec1;
+  __shared__ ChainLocal loc;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+
+  const unsigned nblk = gridDim.x;
+  unsigned bid = blockIdx.x;
+  if (nblk % (8 * NT) == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
+  const int c0 = (int)(bid % NT) * DVT;
+  const int64_t bh = bid / NT;
+  const int64_t nchunks = (p.T + C - 1) / C;
+
+  f4 S[2];  // wavefront w: S^T tiles (d_k block w, d_v block db)
+  {
+    const int lr = l & 15, lg = l >> 4;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int dk = 16 * w + 4 * lg, dv = 16 * db + lr;
+      f4 x = {0.f, 0.f, 0.f, 0.f};
+      if (p.s0) x = *reinterpret_cast<const f4*>(p.s0 + (bh * D + c0 + dv) * D + dk);
+      S[db] = x;
+      *reinterpret_cast<h4*>(sat<D>(&loc.s[0][0], dv, dk)) = to_h4(x);
+    }
+  }
+
+  const Streams sr = make_streams(p, bh, false);
+  const uint8_t* recs = ws + bh * nchunks * kRecBytes;
+  v4u vv = {0u, 0u, 0u, 0u};
+  if (nchunks > 0) {
+    if (tid < 256)
+      vv = __builtin_amdgcn_raw_buffer_load_b128(sr.v, (int)(((tid >> 2) * D + c0 + 8 * (tid & 3)) * 2), 0, 0);
+    fetch_blocks(rec0, recs, w, kRecKiB, NTH / 64, l);
+    if (tid < 256) *reinterpret_cast<h8*>(&loc.v[0][tid >> 2][8 * (tid & 3)]) = bf8_to_h8(vv);
+  }
+  for (int64_t ci = 0; ci < nchunks; ci += 2) {  // buffers by chunk parity; the bounds are uniform
+    chain_chunk<TOut>(rec0, rec1, loc, 0, p, sr, recs, ci, nchunks, bh, c0, tid, w, l, S, vv);
+    if (ci + 1 < nchunks) chain_chunk<TOut>(rec1, rec0, loc, 1, p, sr, recs, ci + 1, nchunks, bh, c0, tid, w, l, S, vv);
+  }
+
+  if (p.s_final) {
+    const int lr = l & 15, lg = l >> 4;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int dk = 16 * w + 4 * lg, dv = 16 * db + lr;
+      *reinterpret_cast<f4*>(p.s_final + (bh * D + c0 + dv) * D + dk) = S[db];
+    }
+  }
+}
+
 }  // namespace
 
 size_t kda_workspace_bytes(const ChunkArgs& a) {
@@ -749,7 +910,6 @@ hipError_t launch_kda_mfma(const ChunkArgs& a, hipStream_t s) {
   const int64_t nchunks = (a.T + C - 1) / C;
   const size_t need = kda_workspace_bytes(a);
   const bool two = a.workspace && need > 0 && a.workspace_bytes >= need;
-  const uint8_t* ws = static_cast<const uint8_t*>(a.workspace);
   if (two) {
     const int64_t recs = a.B * a.H * nchunks;
     if (recs > 0x7fffffff) return hipErrorInvalidValue;
@@ -757,15 +917,16 @@ hipError_t launch_kda_mfma(const ChunkArgs& a, hipStream_t s) {
     const int64_t grid = recs < 256 ? recs : 256;
     hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)grid), dim3(NTH), 0, s, a, static_cast<uint8_t*>(a.workspace),
                        nchunks);
+    const uint8_t* ws = static_cast<const uint8_t*>(a.workspace);
     if (a.out_dtype == GDN_BF16)
-      hipLaunchKernelGGL((kda_chunk_mfma_kernel<__hip_bfloat16, true>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
+      hipLaunchKernelGGL((kda_chain_kernel<__hip_bfloat16>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
     else
-      hipLaunchKernelGGL((kda_chunk_mfma_kernel<float, true>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
+      hipLaunchKernelGGL((kda_chain_kernel<float>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
   } else {
     if (a.out_dtype == GDN_BF16)
-      hipLaunchKernelGGL((kda_chunk_mfma_kernel<__hip_bfloat16, false>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
+      hipLaunchKernelGGL((kda_chunk_mfma_kernel<__hip_bfloat16>), dim3((unsigned)blocks), dim3(NTH), 0, s, a);
     else
-      hipLaunchKernelGGL((kda_chunk_mfma_kernel<float, false>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
+      hipLaunchKernelGGL((kda_chunk_mfma_kernel<float>), dim3((unsigned)blocks), dim3(NTH), 0, s, a);
   }
   return hipGetLastError();
 }
