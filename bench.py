@@ -286,7 +286,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gb, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gb / HBM_PEAK_GBS, 4),
                          "traffic": _traffic("kda_chunk_mfma", ["kda_chunk_mfma.hip", "gdn_mfma_common.h"]),
-                         "kernel": "kda_prep_kernel + kda_chunk_mfma_kernel", "algorithmic_bytes": nb},
+                         "kernel": "kda_prep_kernel + kda_chain_kernel", "algorithmic_bytes": nb},
             "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "workspace_MiB": round(ws.numel() / 2**20, 1),
             "single_kernel_ms": round(ms_single, 4)}
