@@ -288,12 +288,183 @@ __global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
   }
 }
 
+
+// ------------------------------------------------------------------------------------------
+// Matrix-core form of draft-token verification (outputs only, the state is not written) for
+// the scalar gate at d = 128 and windows of at most 8 tokens.  The window is one chunk of the
+// chunkwise form ("Hybrid Linear Attention Architecture Design Explained", section 4), with S
+// the state entering the window, k, q normalised when asked, G_t the inclusive prefix of
+// log alpha and gamma_t = e^{G_t}:
+//   r_t = S k_t, p_t = S q_t                          (one fp32 matrix-core product)
+//   x_t = beta_t (v_t - gamma_t r_t)
+//   u_t = x_t - sum_{j<t} beta_t (k_t.k_j) e^{G_t - G_j} u_j
+//   o_t = gamma_t p_t + sum_{j<=t} (q_t.k_j) e^{G_t - G_j} u_j
+// which is the token loop above regrouped: the state products run on v_mfma_f32_16x16x4_f32
+// (full fp32), the W x W algebra per value channel on 32 lanes.  The per-token reductions of
+// the loop form, which bound its instruction issue, are gone.
+//
+// One workgroup per (sequence, value head), four wavefronts; wave w owns value channels
+// 32 w .. 32 w + 31.  Its slice of S^T stays in MFMA accumulator layout for the whole window:
+// tile (j, n) holds S^T[dk = 16 j + 4 (l/16) + i][dv = 32 w + 16 n + l%16] in component i.
+// Used as the B operand of a 16x16x4 product, component i of the tile is the k-block whose
+// four contraction indices are dk = 16 j + 4 kb + i, kb = l/16; the A operand (the window's
+// keys and queries, one row per lane%16) is loaded with the same index pattern, so no
+// transposition is ever needed.  The same A fragments, used as both operands, give the Gram
+// of the window's keys and queries (their norms on its diagonal).
+constexpr int kWinMax = 8;
+// Four consecutive inputs as fp32 (one 8- or 16-byte load), zeros when !live.
+__device__ __forceinline__ void ld4(const float* p, bool live, float (&x)[4]) {
+  f4v y = {0.f, 0.f, 0.f, 0.f};
+  if (live) y = *reinterpret_cast<const f4v*>(p);
+  x[0] = y[0]; x[1] = y[1]; x[2] = y[2]; x[3] = y[3];
+}
+__device__ __forceinline__ void ld4(const __hip_bfloat16* p, bool live, float (&x)[4]) {
+  uint2 y = {0u, 0u};
+  if (live) y = *reinterpret_cast<const uint2*>(p);
+  x[0] = __uint_as_float(y.x << 16); x[1] = __uint_as_float(y.x & 0xffff0000u);
+  x[2] = __uint_as_float(y.y << 16); x[3] = __uint_as_float(y.y & 0xffff0000u);
+}
+template <typename TIn, typename TOut>
+__global__ __launch_bounds__(256, 2) void decode_win_mfma_kernel(DecodeExArgs a) {
+  constexpr int D = 128;
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  __shared__ float gsh[4][16][16];              // Gram of the window's rows [k_0..k_{W-1}, q_0..q_{W-1}]
+  __shared__ float rsh[4][16][33];              // S k_t and S q_t per wave: [row][value channel]
+
+  const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
+  const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
+  const TIn* __restrict__ v = static_cast<const TIn*>(a.v);
+  const TIn* __restrict__ beta = static_cast<const TIn*>(a.beta);
+  const TIn* __restrict__ log_alpha = static_cast<const TIn*>(a.log_alpha);
+  TOut* __restrict__ o = static_cast<TOut*>(a.o);
+
+  const int64_t s = blockIdx.x;  // (sequence, value head); the grid is exactly N H
+  const int64_t n = s / a.H, h = s - n * a.H, hq = h / (a.H / a.Hqk);
+  const int64_t row_slot = a.slots ? static_cast<int64_t>(a.slots[n]) : n;
+  if (row_slot < 0 || row_slot >= a.P) return;  // uniform over the workgroup
+  const int W = static_cast<int>(a.T);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lr = l & 15, lg = l >> 4;
+
+  // the state slice, all loads issued first
+  f4* S = reinterpret_cast<f4*>(a.pool + (row_slot * a.H + h) * D * D);
+  f4 St[8][2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      St[j][nb] = __builtin_nontemporal_load(&S[((32 * w + 16 * nb + lr) * D + 16 * j + 4 * lg) / 4]);
+
+  // A fragments: row lr of [k_0..k_{W-1}, q_0..q_{W-1}, 0..], channels 16 j + 4 lg + i
+  float af[8][4];
+  {
+    const bool live = lr < 2 * W;
+    const int t = lr < W ? lr : (live ? lr - W : 0);
+    const TIn* src = (lr < W ? k : q) + ((n * a.T + t) * a.Hqk + hq) * D + 4 * lg;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ld4(src + 16 * j, live, af[j]);
+  }
+
+  // gates of the window: lane t < W forms beta_t and log alpha_t, every lane then reads them
+  float G[kWinMax], bt[kWinMax];
+  {
+    float b = 0.f, g = 0.f;
+    if (l < W) {
+      const int64_t g0 = (n * a.T + l) * a.H + h;
+      b = ld_in(beta, g0);
+      g = ld_in(log_alpha, g0);
+      if (a.raw_gates) {
+        b = __builtin_amdgcn_rcpf(1.f + __expf(-b));
+        const float x = g + a.dt_bias[h];
+        g = -__expf(a.A_log[h]) * (fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))));  // softplus, no overflow
+      }
+    }
+    float run = 0.f;
+#pragma unroll
+    for (int t = 0; t < kWinMax; ++t) {
+      run += __shfl(g, t, 64);
+      G[t] = run;
+      bt[t] = __shfl(b, t, 64);
+    }
+  }
+
+  // Gram of the rows, and S k_t, S q_t: contraction over the 128 key channels
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  f4 gm = zero, rp[2] = {zero, zero};
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gm = __builtin_amdgcn_mfma_f32_16x16x4f32(af[j][i], af[j][i], gm, 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) rp[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[j][i], St[j][nb][i], rp[nb], 0, 0, 0);
+    }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    gsh[w][4 * lg + e][lr] = gm[e];
+    rsh[w][4 * lg + e][lr] = rp[0][e];
+    rsh[w][4 * lg + e][16 + lr] = rp[1][e];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // normalisation factors 1 / |k_t|, 1 / |q_t| (the Gram's diagonal), every lane
+  float rk[kWinMax], rq[kWinMax];
+#pragma unroll
+  for (int t = 0; t < kWinMax; ++t) {
+    rk[t] = 1.f;
+    rq[t] = 1.f;
+    if (a.qk_l2norm && t < W) {
+      rk[t] = __builtin_amdgcn_rsqf(gsh[w][t][t] + 1e-6f);
+      rq[t] = __builtin_amdgcn_rsqf(gsh[w][W + t][W + t] + 1e-6f);
+    }
+  }
+
+  // per value channel: the substitution and the outputs (lanes 0..31)
+  if (l < 32) {
+    const int dv = 32 * w + l;
+    float u[kWinMax];
+#pragma unroll
+    for (int t = 0; t < kWinMax; ++t) {
+      u[t] = 0.f;
+      if (t >= W) continue;  // uniform
+      const int64_t tok = n * a.T + t;
+      const float gam = __expf(G[t]);
+      float x = bt[t] * (ld_in(v, (tok * a.H + h) * D + dv) - gam * rk[t] * rsh[w][t][l]);
+      float dq[kWinMax];  // e^{G_t - G_j} / |k_j|, j <= t
+#pragma unroll
+      for (int j = 0; j <= t; ++j) dq[j] = __expf(G[t] - G[j]) * rk[j];
+      const float ct = bt[t] * rk[t];
+#pragma unroll
+      for (int j = 0; j < t; ++j) x -= ct * gsh[w][t][j] * dq[j] * u[j];
+      u[t] = x;
+      float y = 0.f;
+#pragma unroll
+      for (int j = 0; j <= t; ++j) y += gsh[w][W + t][j] * dq[j] * u[j];
+      st_out(o, (tok * a.H + h) * D + dv, rq[t] * (gam * rsh[w][W + t][l] + y));
+    }
+  }
+}
+
 template <int D, typename TIn, typename TOut>
 hipError_t launch_decode_ex_t(const DecodeExArgs& a, hipStream_t stream) {
   constexpr int SPB = kThreads / (2 * D);
   const int64_t units = a.N * a.H;
   const int64_t blocks = (units + SPB - 1) / SPB;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if constexpr (D == 128) {
+    // Verification windows (outputs only) take the matrix-core form.  A window that writes the
+    // state stays on the row-coalesced kernel: reading and writing every state is HBM-bound
+    // there already, and the accumulator layout moves the state in 64-byte pieces per row.
+    if (!a.kda && !a.write_state && a.o && a.T <= kWinMax && units <= 0x7fffffff) {
+      hipLaunchKernelGGL((decode_win_mfma_kernel<TIn, TOut>), dim3(static_cast<unsigned>(units)), dim3(256), 0,
+                         stream, a);
+      return hipGetLastError();
+    }
+  }
   if (a.kda)
     hipLaunchKernelGGL((decode_ex_kernel<D, TIn, TOut, true>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
                        stream, a);

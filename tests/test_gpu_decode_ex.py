@@ -140,10 +140,11 @@ def test_verify_workload_full_size_sampled():
     assert torch.equal(d["pool"][torch.as_tensor(unused)], pool0[torch.as_tensor(unused)])
 
 
-@pytest.mark.parametrize("T", [2, 4, 5, 8])
+@pytest.mark.parametrize("T", [1, 2, 4, 5, 8, 9])
 @pytest.mark.parametrize("kda,raw", [(False, False), (True, False), (False, True)])
 def test_window_lengths_d128(T, kda, raw):
-    """Windows of 2, 4, 5 and 8 tokens at d = 128, plain, KDA and with the fused prologue."""
+    """Windows of 1 to 9 tokens at d = 128, plain, KDA and with the fused prologue (verification
+    of up to 8 tokens runs on the matrix cores, longer windows and commits token by token)."""
     import gated_deltanet_state_amd as g
     N, H, Hqk, D, P = 6, 4, 2, 128, 9
     say(f"decode_ex d128 T={T} kda={kda} raw={raw}")
