@@ -310,7 +310,8 @@ __global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
 // four contraction indices are dk = 16 j + 4 kb + i, kb = l/16; the A operand (the window's
 // keys and queries, one row per lane%16) is loaded with the same index pattern, so no
 // transposition is ever needed.  The same A fragments, used as both operands, give the Gram
-// of the window's keys and queries (their norms on its diagonal).
+// of the window's keys and queries (their norms on its diagonal); each wave forms it over a
+// quarter of the key channels and the four parts are summed through LDS.
 constexpr int kWinMax = 8;
 // Four consecutive inputs as fp32 (one 8- or 16-byte load), zeros when !live.
 __device__ __forceinline__ void ld4(const float* p, bool live, float (&x)[4]) {
@@ -328,6 +329,7 @@ template <typename TIn, typename TOut>
 __global__ __launch_bounds__(256, 2) void decode_win_mfma_kernel(DecodeExArgs a) {
   constexpr int D = 128;
   typedef float f4 __attribute__((ext_vector_type(4)));
+  __shared__ float gpart[4][16][16];            // per wave: Gram over its quarter of the key channels
   __shared__ float gsh[4][16][16];              // Gram of the window's rows [k_0..k_{W-1}, q_0..q_{W-1}]
   __shared__ float rsh[4][16][33];              // S k_t and S q_t per wave: [row][value channel]
 
@@ -397,15 +399,21 @@ __global__ __launch_bounds__(256, 2) void decode_win_mfma_kernel(DecodeExArgs a)
   for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      gm = __builtin_amdgcn_mfma_f32_16x16x4f32(af[j][i], af[j][i], gm, 0, 0, 0);
+      if (j >> 1 == w) gm = __builtin_amdgcn_mfma_f32_16x16x4f32(af[j][i], af[j][i], gm, 0, 0, 0);  // uniform
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) rp[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[j][i], St[j][nb][i], rp[nb], 0, 0, 0);
     }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    gsh[w][4 * lg + e][lr] = gm[e];
+    gpart[w][4 * lg + e][lr] = gm[e];
     rsh[w][4 * lg + e][lr] = rp[0][e];
     rsh[w][4 * lg + e][16 + lr] = rp[1][e];
+  }
+  __syncthreads();  // the four parts of the Gram
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * lg + e;
+    gsh[w][r][lr] = (gpart[0][r][lr] + gpart[1][r][lr]) + (gpart[2][r][lr] + gpart[3][r][lr]);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
