@@ -388,7 +388,8 @@ def main():
                  "roofline": {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(gb / HBM_PEAK_GBS, 4),
                               "traffic": _traffic(f"decode_ex_{phase}", ["gdn_decode.hip"]),
-                              "kernel": "decode_ex_kernel", "algorithmic_bytes": int(nb)}}
+                              "kernel": "decode_win_mfma_kernel" if phase == "verify" else "decode_ex_kernel",
+                              "algorithmic_bytes": int(nb)}}
             r.update(more)
             log(f"serving {name}: {ms * 1e3:.1f} us, {gb:.0f} GB/s, HBM frac {gb / HBM_PEAK_GBS:.3f}")
             return r
