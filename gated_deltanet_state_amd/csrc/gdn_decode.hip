@@ -326,9 +326,10 @@ __device__ __forceinline__ void ld4(const __hip_bfloat16* p, bool live, float (&
   x[2] = __uint_as_float(y.y << 16); x[3] = __uint_as_float(y.y & 0xffff0000u);
 }
 template <typename TIn, typename TOut>
-__global__ __launch_bounds__(256, 2) void decode_win_mfma_kernel(DecodeExArgs a) {
+__global__ __launch_bounds__(256, 5) void decode_win_mfma_kernel(DecodeExArgs a) {
   constexpr int D = 128;
   typedef float f4 __attribute__((ext_vector_type(4)));
+  __shared__ float ash[16][D + 8];              // rows [k_0..k_{W-1}, q_0..q_{W-1}, 0..] (8-bank row skew)
   __shared__ float gpart[4][16][16];            // per wave: Gram over its quarter of the key channels
   __shared__ float gsh[4][16][16];              // Gram of the window's rows [k_0..k_{W-1}, q_0..q_{W-1}]
   __shared__ float rsh[4][16][33];              // S k_t and S q_t per wave: [row][value channel]
@@ -359,50 +360,43 @@ __global__ __launch_bounds__(256, 2) void decode_win_mfma_kernel(DecodeExArgs a)
     for (int nb = 0; nb < 2; ++nb)
       St[j][nb] = __builtin_nontemporal_load(&S[((32 * w + 16 * nb + lr) * D + 16 * j + 4 * lg) / 4]);
 
-  // A fragments: row lr of [k_0..k_{W-1}, q_0..q_{W-1}, 0..], channels 16 j + 4 lg + i
-  float af[8][4];
+  // the window's key and query rows, staged once for the four waves: thread tid holds
+  // channels 8 (tid % 16) .. + 7 of row tid / 16
   {
-    const bool live = lr < 2 * W;
-    const int t = lr < W ? lr : (live ? lr - W : 0);
-    const TIn* src = (lr < W ? k : q) + ((n * a.T + t) * a.Hqk + hq) * D + 4 * lg;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ld4(src + 16 * j, live, af[j]);
+    const int r = tid >> 4, c = 8 * (tid & 15);
+    const bool live = r < 2 * W;
+    const int t = r < W ? r : (live ? r - W : 0);
+    const TIn* src = (r < W ? k : q) + ((n * a.T + t) * a.Hqk + hq) * D + c;
+    float x[4], y[4];
+    ld4(src, live, x);
+    ld4(src + 4, live, y);
+    *reinterpret_cast<f4*>(&ash[r][c]) = f4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f4*>(&ash[r][c + 4]) = f4{y[0], y[1], y[2], y[3]};
   }
 
-  // gates of the window: lane t < W forms beta_t and log alpha_t, every lane then reads them
-  float G[kWinMax], bt[kWinMax];
-  {
-    float b = 0.f, g = 0.f;
-    if (l < W) {
-      const int64_t g0 = (n * a.T + l) * a.H + h;
-      b = ld_in(beta, g0);
-      g = ld_in(log_alpha, g0);
-      if (a.raw_gates) {
-        b = __builtin_amdgcn_rcpf(1.f + __expf(-b));
-        const float x = g + a.dt_bias[h];
-        g = -__expf(a.A_log[h]) * (fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))));  // softplus, no overflow
-      }
-    }
-    float run = 0.f;
-#pragma unroll
-    for (int t = 0; t < kWinMax; ++t) {
-      run += __shfl(g, t, 64);
-      G[t] = run;
-      bt[t] = __shfl(b, t, 64);
-    }
+  // gates of the window: lane t < W loads beta_t and log alpha_t (formed after the products)
+  float gb = 0.f, gg = 0.f;
+  if (l < W) {
+    const int64_t g0 = (n * a.T + l) * a.H + h;
+    gb = ld_in(beta, g0);
+    gg = ld_in(log_alpha, g0);
   }
 
-  // Gram of the rows, and S k_t, S q_t: contraction over the 128 key channels
+  // Gram of the rows, and S k_t, S q_t: contraction over the 128 key channels.  A fragment:
+  // row l%16, channels 16 j + 4 (l/16) .. + 3 (one conflict-free 16-byte read per j).
+  __syncthreads();  // the rows are staged
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
   f4 gm = zero, rp[2] = {zero, zero};
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < 8; ++j) {
+    const f4 af = *reinterpret_cast<const f4*>(&ash[lr][16 * j + 4 * lg]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (j >> 1 == w) gm = __builtin_amdgcn_mfma_f32_16x16x4f32(af[j][i], af[j][i], gm, 0, 0, 0);  // uniform
+      if (j >> 1 == w) gm = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], af[i], gm, 0, 0, 0);  // uniform
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) rp[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[j][i], St[j][nb][i], rp[nb], 0, 0, 0);
+      for (int nb = 0; nb < 2; ++nb) rp[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], St[j][nb][i], rp[nb], 0, 0, 0);
     }
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     gpart[w][4 * lg + e][lr] = gm[e];
@@ -418,6 +412,23 @@ __global__ __launch_bounds__(256, 2) void decode_win_mfma_kernel(DecodeExArgs a)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // gates: lane t < W forms beta_t and log alpha_t, every lane then reads them
+  float G[kWinMax], bt[kWinMax];
+  {
+    if (a.raw_gates && l < W) {
+      gb = __builtin_amdgcn_rcpf(1.f + __expf(-gb));
+      const float x = gg + a.dt_bias[h];
+      gg = -__expf(a.A_log[h]) * (fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))));  // softplus, no overflow
+    }
+    float run = 0.f;
+#pragma unroll
+    for (int t = 0; t < kWinMax; ++t) {
+      run += __shfl(gg, t, 64);
+      G[t] = run;
+      bt[t] = __shfl(gb, t, 64);
+    }
+  }
 
   // normalisation factors 1 / |k_t|, 1 / |q_t| (the Gram's diagonal), every lane
   float rk[kWinMax], rq[kWinMax];
