@@ -683,6 +683,7 @@ struct alignas(16) ChainLocal {
   alignas(16) _Float16 s[DVT][D];           // fp16 copy of the state slice [d_v][d_k], swizzled (128-wide)
   alignas(16) _Float16 v[2][C][DVT + 8];    // value slice [token][d_v], by chunk parity
   alignas(16) _Float16 u[DVT][C];           // U [d_v][token], swizzled (64-wide)
+  alignas(16) f4 x[4][2][64];               // X tiles (token block, value block), lane-major
 };
 static_assert(2 * sizeof(KdaRec) + sizeof(ChainLocal) <= 160 * 1024, "LDS budget");
 
@@ -704,7 +705,7 @@ __device__ __forceinline__ void fetch_blocks(KdaRec& dst, const uint8_t* src, in
 // Split of the next record's copy: waves 2..7 take blocks below kSplit during the substitution
 // (which runs on waves 0 and 1 alone); waves 0 and 1 take the rest at the end of the chunk,
 // where they finish earlier than the output waves.
-constexpr int kSplit = 50;
+constexpr int kSplit = kRecKiB;
 static_assert(kSplit <= kRecKiB, "copy split");
 
 // One chunk: record rc (already in LDS), values in loc.v[vb].  Issues the copy of the next
@@ -722,43 +723,26 @@ __device__ __forceinline__ void chain_chunk(const KdaRec& rc, KdaRec& nx, ChainL
   if (more && tid < 256)
     vv = __builtin_amdgcn_raw_buffer_load_b128(sr.v, (int)((((ci + 1) * C + (tid >> 2)) * D + c0 + 8 * (tid & 3)) * 2), 0, 0);
 
-  // ---- phase 1: X (waves 0,1), O = (Q Gamma) S^T tiles (waves 2..7)
+  // ---- phase 1: one X tile and one O^T = S (Q Gamma)^T tile per wave: token block i = w / 2,
+  // value block db = w % 2 (one read of the state fragment serves both)
   l = opaque(l);
   int lr = l & 15, lg = l >> 4;
-  f4 X[4], Oacc[2];
-  if (w < 2) {
-    const int db = w, dv = 16 * db + lr;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) X[i] = f4{0.f, 0.f, 0.f, 0.f};
+  f4 oa;
+  {
+    const int i = w >> 1, db = w & 1, dv = 16 * db + lr;
+    f4 x = {0.f, 0.f, 0.f, 0.f};
+    oa = x;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const h8 sb = sfrag8<D>(&loc.s[0][0], 16 * db, 32 * kk, l);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) X[i] = mfma32(sfrag8<D>(&rc.kl[0][0], 16 * i, 32 * kk, l), sb, X[i]);
+      x = mfma32(sfrag8<D>(&rc.kl[0][0], 16 * i, 32 * kk, l), sb, x);
+      oa = mfma32(sb, sfrag8<D>(&rc.ql[0][0], 16 * i, 32 * kk, l), oa);
     }
+    const int c = 16 * i + 4 * lg;
+    const f4 be = *reinterpret_cast<const f4*>(&rc.beta[c]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = 16 * i + 4 * lg;
-      const f4 be = *reinterpret_cast<const f4*>(&rc.beta[c]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) X[i][e] = be[e] * ((float)loc.v[vb][c + e][dv] - X[i][e]);
-    }
-  } else {
-    const int no = o_count(w);
-    f4 acc[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        if (t2 >= no) continue;
-        int cb, db;
-        o_tile(w, t2, cb, db);
-        acc[t2] = mfma32(sfrag8<D>(&loc.s[0][0], 16 * db, 32 * kk, l), sfrag8<D>(&rc.ql[0][0], 16 * cb, 32 * kk, l),
-                         acc[t2]);
-      }
-    }
-    Oacc[0] = acc[0];
-    Oacc[1] = acc[1];
+    for (int e = 0; e < 4; ++e) x[e] = be[e] * ((float)loc.v[vb][c + e][dv] - x[e]);
+    loc.x[i][db][l] = x;
   }
   phase_barrier();
 
@@ -772,8 +756,10 @@ __device__ __forceinline__ void chain_chunk(const KdaRec& rc, KdaRec& nx, ChainL
   if (w < 2) {
     const int dv = 16 * w + lr;
     h4 an[6], tdf[4];
+    f4 X[4];
 #pragma unroll
     for (int i = 0, m = 0; i < 4; ++i) {
+      X[i] = loc.x[i][w][l];
       tdf[i] = frag4(&rc.td[i][0][0], 16, 0, 0, l);
 #pragma unroll
       for (int j = 0; j < i; ++j, ++m) an[m] = frag4(&rc.an[m][0][0], 16, 0, 0, l);
@@ -793,23 +779,17 @@ __device__ __forceinline__ void chain_chunk(const KdaRec& rc, KdaRec& nx, ChainL
   // ---- phase 3: O += U^T P^T, output (waves 2..7); S <- S Diag(Gamma_63) + U^T (K e^{G_63 - G})
   l = opaque(l);
   lr = l & 15, lg = l >> 4;
-  if (w >= 2) {
+  {
     TOut* O = static_cast<TOut*>(p.o);
-    const int no = o_count(w);
+    const int cb = w >> 1, db = w & 1;
+    f4 acc = oa;
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      if (t2 >= no) continue;
-      int cb, db;
-      o_tile(w, t2, cb, db);
-      f4 acc = Oacc[t2];
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        if (kc == 1 && cb < 2) continue;
-        acc = mfma32(sfrag8<C>(&loc.u[0][0], 16 * db, 32 * kc, l), sfrag8<C>(&rc.p[0][0], 16 * cb, 32 * kc, l), acc);
-      }
-      const int c = 16 * cb + lr;
-      if (c < n) store_o4<TOut>(O, (bh * T + t0 + c) * D + c0 + 16 * db + 4 * lg, acc);
+    for (int kc = 0; kc < 2; ++kc) {
+      if (kc == 1 && cb < 2) continue;
+      acc = mfma32(sfrag8<C>(&loc.u[0][0], 16 * db, 32 * kc, l), sfrag8<C>(&rc.p[0][0], 16 * cb, 32 * kc, l), acc);
     }
+    const int c = 16 * cb + lr;
+    if (c < n) store_o4<TOut>(O, (bh * T + t0 + c) * D + c0 + 16 * db + 4 * lg, acc);
   }
   {
     // The snapshot store goes through a buffer descriptor whose range is empty when no snapshot
