@@ -326,13 +326,19 @@ __device__ __forceinline__ void ld4(const __hip_bfloat16* p, bool live, float (&
   x[2] = __uint_as_float(y.y << 16); x[3] = __uint_as_float(y.y & 0xffff0000u);
 }
 template <typename TIn, typename TOut>
-__global__ __launch_bounds__(256, 5) void decode_win_mfma_kernel(DecodeExArgs a) {
+__global__ __launch_bounds__(256, 8) void decode_win_mfma_kernel(DecodeExArgs a) {
   constexpr int D = 128;
   typedef float f4 __attribute__((ext_vector_type(4)));
-  __shared__ float ash[16][D + 8];              // rows [k_0..k_{W-1}, q_0..q_{W-1}, 0..] (8-bank row skew)
+  // The staged rows are dead once the products are done; S k_t, S q_t reuse their space (written
+  // after the barrier that follows the products).
+  __shared__ union {
+    float ash[16][D + 8];                       // rows [k_0..k_{W-1}, q_0..q_{W-1}, 0..] (8-bank row skew)
+    float rsh[4][16][33];                       // S k_t and S q_t per wave: [row][value channel]
+  } lu;
   __shared__ float gpart[4][16][16];            // per wave: Gram over its quarter of the key channels
   __shared__ float gsh[4][16][16];              // Gram of the window's rows [k_0..k_{W-1}, q_0..q_{W-1}]
-  __shared__ float rsh[4][16][33];              // S k_t and S q_t per wave: [row][value channel]
+  auto& ash = lu.ash;
+  auto& rsh = lu.rsh;
 
   const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
   const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
@@ -351,14 +357,11 @@ __global__ __launch_bounds__(256, 5) void decode_win_mfma_kernel(DecodeExArgs a)
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lg = l >> 4;
 
-  // the state slice, all loads issued first
+  // the first 16 rows of the state slice (the second half is loaded once these are used)
   f4* S = reinterpret_cast<f4*>(a.pool + (row_slot * a.H + h) * D * D);
-  f4 St[8][2];
+  f4 St[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      St[j][nb] = __builtin_nontemporal_load(&S[((32 * w + 16 * nb + lr) * D + 16 * j + 4 * lg) / 4]);
+  for (int j = 0; j < 8; ++j) St[j] = __builtin_nontemporal_load(&S[((32 * w + lr) * D + 16 * j + 4 * lg) / 4]);
 
   // the window's key and query rows, staged once for the four waves: thread tid holds
   // channels 8 (tid % 16) .. + 7 of row tid / 16
@@ -388,26 +391,31 @@ __global__ __launch_bounds__(256, 5) void decode_win_mfma_kernel(DecodeExArgs a)
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
   f4 gm = zero, rp[2] = {zero, zero};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const f4 af = *reinterpret_cast<const f4*>(&ash[lr][16 * j + 4 * lg]);
+  for (int nb = 0; nb < 2; ++nb) {  // 16-row halves of the slice, one after the other
+    if (nb == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (j >> 1 == w) gm = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], af[i], gm, 0, 0, 0);  // uniform
+      for (int j = 0; j < 8; ++j)
+        St[j] = __builtin_nontemporal_load(&S[((32 * w + 16 + lr) * D + 16 * j + 4 * lg) / 4]);
+    }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) rp[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], St[j][nb][i], rp[nb], 0, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+      const f4 af = *reinterpret_cast<const f4*>(&ash[lr][16 * j + 4 * lg]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (nb == 0 && j >> 1 == w) gm = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], af[i], gm, 0, 0, 0);  // uniform
+        rp[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], St[j][i], rp[nb], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    gpart[w][4 * lg + e][lr] = gm[e];
-    rsh[w][4 * lg + e][lr] = rp[0][e];
-    rsh[w][4 * lg + e][16 + lr] = rp[1][e];
-  }
-  __syncthreads();  // the four parts of the Gram
+  for (int e = 0; e < 4; ++e) gpart[w][4 * lg + e][lr] = gm[e];
+  __syncthreads();  // the four parts of the Gram; every wave is done with the staged rows
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int r = 4 * lg + e;
     gsh[w][r][lr] = (gpart[0][r][lr] + gpart[1][r][lr]) + (gpart[2][r][lr] + gpart[3][r][lr]);
+    rsh[w][r][lr] = rp[0][e];
+    rsh[w][r][16 + lr] = rp[1][e];
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
