@@ -304,8 +304,9 @@ __global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
 // the loop form, which bound its instruction issue, are gone.
 //
 // One workgroup per (sequence, value head), four wavefronts; wave w owns value channels
-// 32 w .. 32 w + 31.  Its slice of S^T stays in MFMA accumulator layout for the whole window:
-// tile (j, n) holds S^T[dk = 16 j + 4 (l/16) + i][dv = 32 w + 16 n + l%16] in component i.
+// 32 w .. 32 w + 31.  Its slice of S^T is read straight into MFMA accumulator layout, one
+// 16-row half n at a time (fewer live registers, more waves per SIMD): tile j of half n holds
+// S^T[dk = 16 j + 4 (l/16) + i][dv = 32 w + 16 n + l%16] in component i.
 // Used as the B operand of a 16x16x4 product, component i of the tile is the k-block whose
 // four contraction indices are dk = 16 j + 4 kb + i, kb = l/16; the A operand (the window's
 // keys and queries, one row per lane%16) is loaded with the same index pattern, so no
