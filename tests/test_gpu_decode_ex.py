@@ -160,3 +160,28 @@ def test_window_lengths_d128(T, kda, raw):
     live = _live(inp)
     assert rel_l2(o[torch.as_tensor(live)], o_ref[live]) <= 1e-5
     assert rel_l2(d["pool"], pool_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("T", [3, 8])
+def test_verify_l2norm_plain_gates_one_qk_head(T):
+    """Verification with the q/k normalisation but plain gates, q and k rows far from unit
+    length, all four value heads reading one query/key head, bf16 outputs."""
+    import gated_deltanet_state_amd as g
+    N, H, Hqk, D, P = 6, 4, 1, 128, 8
+    say(f"decode_ex verify l2norm plain gates T={T}")
+    inp = synth.make_serving(N, T, H, Hqk, D, P, torch.bfloat16, seed=70 + T, skip_every=5)
+    inp["q"] = (inp["q"].float() * 2.5).to(torch.bfloat16)
+    inp["k"] = (inp["k"].float() * 0.4).to(torch.bfloat16)
+    d = _cuda(inp)
+    o = g.gdn_decode_verify(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], slots=d["slots"],
+                            qk_l2norm=True, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    o_ref, _ = _ref(inp, kda=False, raw=False, write_state=False, l2=True)
+    live = _live(inp)
+    assert rel_l2(o[torch.as_tensor(live)], o_ref[live]) <= 2e-3
+    # without the normalisation the same rows give other outputs
+    o_raw = g.gdn_decode_verify(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], slots=d["slots"],
+                                out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert rel_l2(o_raw[torch.as_tensor(live)], o_ref[live]) > 1e-2
