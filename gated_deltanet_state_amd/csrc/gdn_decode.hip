@@ -487,7 +487,10 @@ hipError_t launch_decode_ex_t(const DecodeExArgs& a, hipStream_t stream) {
     // Verification windows (outputs only) take the matrix-core form.  A window that writes the
     // state stays on the row-coalesced kernel: reading and writing every state is HBM-bound
     // there already, and the accumulator layout moves the state in 64-byte pieces per row.
-    if (!a.kda && !a.write_state && a.o && a.T <= kWinMax && units <= 0x7fffffff) {
+    // its key/query loads move 4 elements at once: the bases must be aligned to that
+    const uintptr_t qk_align = 4 * sizeof(TIn);
+    const bool qk_aligned = (reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k)) % qk_align == 0;
+    if (!a.kda && !a.write_state && a.o && a.T <= kWinMax && qk_aligned && units <= 0x7fffffff) {
       hipLaunchKernelGGL((decode_win_mfma_kernel<TIn, TOut>), dim3(static_cast<unsigned>(units)), dim3(256), 0,
                          stream, a);
       return hipGetLastError();

@@ -185,3 +185,31 @@ def test_verify_l2norm_plain_gates_one_qk_head(T):
                                 out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert rel_l2(o_raw[torch.as_tensor(live)], o_ref[live]) > 1e-2
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_verify_misaligned_qk_views(dtype):
+    """q and k passed as views one element past an aligned address (allowed by the ABI, which
+    asks only for element alignment) give the same outputs as aligned copies, to rounding."""
+    import gated_deltanet_state_amd as g
+    N, T, H, D, P = 5, 4, 2, 128, 6
+    say(f"decode_ex verify misaligned q/k dtype={dtype}")
+    inp = synth.make_serving(N, T, H, H, D, P, dtype, seed=91)
+    d = _cuda(inp)
+
+    def shifted(x):
+        buf = torch.empty(x.numel() + 1, dtype=x.dtype, device=x.device)
+        view = buf[1:].view(x.shape)
+        view.copy_(x)
+        return view
+
+    qs, ks = shifted(d["q"]), shifted(d["k"])
+    assert qs.data_ptr() % 16 != 0 and ks.data_ptr() % 16 != 0
+    o_a = g.gdn_decode_verify(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], out_dtype=torch.float32)
+    o_m = g.gdn_decode_verify(d["pool"], qs, ks, d["v"], d["beta"], d["log_alpha"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, _ = _ref(dict(inp, slots=torch.arange(N, dtype=torch.int32)), kda=False, raw=False, write_state=False,
+                    l2=False)
+    tol = 1e-5 if dtype == torch.float32 else 2e-3
+    assert rel_l2(o_m, o_ref) <= tol and rel_l2(o_a, o_ref) <= tol
+    assert rel_l2(o_m, o_a) <= 1e-5
