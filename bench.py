@@ -313,7 +313,8 @@ def main():
             "workload": "gdn_prefill_grouped32x16_rawgates_qknorm_bf16", "B": B, "H": H, "H_qk": Hqk, "T": T, "d": D,
             "us": round(ms * 1e3, 2), "Mtok_per_s": round(B * T / (ms * 1e-3) / 1e6, 3),
             "roofline": {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gb / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(gb / HBM_PEAK_GBS, 4),
+                         "traffic": _traffic("gdn_chunk_mfma_prologue", ["gdn_chunk_mfma.hip", "gdn_mfma_common.h"]),
                          "kernel": "gdn_chunk_mfma_kernel", "algorithmic_bytes": int(nb)},
             "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         log(f"prefill_ex: {ms * 1e3:.1f} us, {gb:.0f} GB/s")
@@ -340,7 +341,8 @@ def main():
             "lengths": f"uniform 256..1792 (seeded), min {min(lens)}, max {max(lens)}",
             "us": round(ms * 1e3, 2), "Mtok_per_s": round(T / (ms * 1e-3) / 1e6, 3),
             "roofline": {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gb / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(gb / HBM_PEAK_GBS, 4),
+                         "traffic": _traffic("gdn_chunk_mfma_ragged", ["gdn_chunk_mfma.hip", "gdn_mfma_common.h"]),
                          "kernel": "gdn_chunk_mfma_kernel", "algorithmic_bytes": int(nb)}}
         log(f"prefill_ragged: {T} tokens in {ms * 1e3:.1f} us, {T / (ms * 1e-3) / 1e6:.1f} Mtok/s")
         del d, s0, cu
