@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 111 /* 1.1.1 */
+#define GDN_VERSION 112 /* 1.1.2 */
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
 
@@ -234,7 +234,11 @@ gdn_status_t gdn_decode_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv, gdn_d
  *   o         [N, T, H, Dv] out_dtype, output of every token of the window, or NULL (then
  *             the kernel stops after the committed tokens).  Rows of skipped sequences are
  *             not written.
- * Token t of a sequence sees the state after its tokens 0..t-1 of this window.  Supported:
+ * Token t of a sequence sees the state after its tokens 0..t-1 of this window.  A window
+ * that only verifies (write_state = 0, o given) with kda = 0, Dk = 128, T <= 8 and q, k
+ * aligned to 4 elements is computed as one chunk of the chunkwise form on the fp32 matrix
+ * cores; its outputs agree with the token-by-token result to fp32 rounding, not bit for bit.
+ * Supported:
  * Dk == Dv in {16, 32, 64, 128}; raw_gates with kda is NOT_SUPPORTED.  Two sequences
  * must not share a slot in one call (their writes would race).  N = 0, or o = NULL with
  * write_state = 0, is a no-op.

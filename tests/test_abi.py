@@ -43,7 +43,7 @@ def test_desc_struct_layout(g):
 
 
 def test_version_and_status_strings(g):
-    assert g.gdn_version() == 111
+    assert g.gdn_version() == 112
     for s in range(4):
         assert isinstance(g.gdn_status_string(s), str) and g.gdn_status_string(s)
     assert g.gdn_status_string(99) == "unknown status"
