@@ -193,7 +193,7 @@ def test_kda_mfma_snapshots_resume_empty():
     assert o.shape == (1, 2, 0, 128) and torch.equal(sf.cpu(), e["s0"])
 
 
-@pytest.mark.parametrize("T,every", [(200, 0), (256, 64), (1, 0)])
+@pytest.mark.parametrize("T,every", [(200, 0), (256, 64), (1, 0), (1000, 0), (1984, 320)])
 def test_kda_two_kernel_form_is_the_single_kernel(T, every):
     """With its workspace the KDA prefill computes every chunk's state-independent tiles in a
     separate parallel kernel; the sequential kernel then runs the same arithmetic on the same
