@@ -358,11 +358,14 @@ __global__ __launch_bounds__(256, 8) void decode_win_mfma_kernel(DecodeExArgs a)
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lg = l >> 4;
 
-  // the first 16 rows of the state slice (the second half is loaded once these are used)
+  // the first 16 rows of the state slice (the second half is loaded once these are used).
+  // Ordinary loads: each 128-byte line is read as two 64-byte halves by consecutive
+  // instructions, and with the non-temporal hint the line can leave the cache in between
+  // and be fetched twice.
   f4* S = reinterpret_cast<f4*>(a.pool + (row_slot * a.H + h) * D * D);
   f4 St[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) St[j] = __builtin_nontemporal_load(&S[((32 * w + lr) * D + 16 * j + 4 * lg) / 4]);
+  for (int j = 0; j < 8; ++j) St[j] = S[((32 * w + lr) * D + 16 * j + 4 * lg) / 4];
 
   // the window's key and query rows, staged once for the four waves: thread tid holds
   // channels 8 (tid % 16) .. + 7 of row tid / 16
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(256, 8) void decode_win_mfma_kernel(DecodeExArgs a)
     if (nb == 1) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        St[j] = __builtin_nontemporal_load(&S[((32 * w + 16 + lr) * D + 16 * j + 4 * lg) / 4]);
+        St[j] = S[((32 * w + 16 + lr) * D + 16 * j + 4 * lg) / 4];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
