@@ -111,12 +111,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ st
   const int c4 = lt % LPR;                // column quad, and the lane's index inside its row group
   const int rg = lt / LPR;
 
-  // the states stream through once per step: non-temporal loads and stores keep them from
-  // displacing the small per-token inputs in the caches
+  // the states stream through once per step. Ordinary loads (the non-temporal hint on the
+  // loads measured about 12% slower for the same bytes); the stores stay non-temporal (plain
+  // stores measured about 25% slower)
   f4v* S = reinterpret_cast<f4v*>(state + s * D * D);
   f4v st[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(&S[(rg + RG * i) * LPR + c4]);
+  for (int i = 0; i < RPT; ++i) st[i] = S[(rg + RG * i) * LPR + c4];
 
   float kk[4], qq[4];
 #pragma unroll
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
   f4v* S = reinterpret_cast<f4v*>(a.pool + (row_slot * a.H + h) * D * D);
   f4v st[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) st[i] = __builtin_nontemporal_load(&S[(rg + RG * i) * LPR + c4]);
+  for (int i = 0; i < RPT; ++i) st[i] = S[(rg + RG * i) * LPR + c4];
   float A = 0.f, dtb = 0.f;
   if (!KDA && a.raw_gates) {
     A = __expf(a.A_log[h]);
