@@ -369,8 +369,10 @@ def main():
 
         ms_c = time_launches(commit, 20, 3, torch)
         nc = inp["n_commit"].numpy()
-        # a sequence with no accepted token needs neither its state nor its inputs
-        nb_c = int(2 * (nc > 0).sum() * cv.H * state_b + nc.sum() * tok_in + 2 * cv.H * 4 + 2 * cv.N * 4)
+        # a sequence with no accepted token needs neither its state nor its inputs; a commit
+        # produces no outputs and so reads no queries
+        tok_in_c = tok_in - cv.Hqk * cv.D * 2
+        nb_c = int(2 * (nc > 0).sum() * cv.H * state_b + nc.sum() * tok_in_c + 2 * cv.H * 4 + 2 * cv.N * 4)
         del d, o, inp
         torch.cuda.empty_cache()
         ck = synth.SERVING["kda"]

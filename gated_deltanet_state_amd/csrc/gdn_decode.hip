@@ -175,8 +175,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ st
 //     Attention to hybrid ones", section 7); the step is then the scalar one with alpha = 1.
 // The state is read once and, on commit, written once: the tokens of the window run on the
 // registers, each with the reductions of the single-step kernel above.  The state after the
-// last committed token is stored as soon as it exists.
-template <int D, typename TIn, typename TOut, bool KDA>
+// last committed token is stored as soon as it exists.  Without outputs (OUT false: commit
+// alone) only the key products S k are formed and reduced.
+template <int D, typename TIn, typename TOut, bool KDA, bool OUT>
 __global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
   constexpr int LPR = D / 4, RG = 8, TPS = LPR * RG, SPB = kThreads / TPS, RPT = D / RG;
   static_assert(2 * RPT == LPR, "one reduced value per lane");
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
     ncommit = a.n_commit ? a.n_commit[n] : static_cast<int>(a.T);
     ncommit = ncommit < 0 ? 0 : (ncommit > a.T ? static_cast<int>(a.T) : ncommit);
   }
-  const int tend = o ? static_cast<int>(a.T) : ncommit;
+  const int tend = OUT ? static_cast<int>(a.T) : ncommit;
   if (tend == 0) return;
 
   const int lt = tid % TPS, c4 = lt % LPR, rg = lt / LPR;
@@ -218,20 +219,22 @@ __global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
   for (int t = 0; t < tend; ++t) {
     const int64_t tok = n * a.T + t;
     const int64_t qk0 = (tok * a.Hqk + hq) * D, g0 = tok * a.H + h;
-    float kk[4], qq[4];
+    float kk[4], qq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       kk[j] = ld_in(k, qk0 + 4 * c4 + j);
-      qq[j] = ld_in(q, qk0 + 4 * c4 + j);
+      if constexpr (OUT) qq[j] = ld_in(q, qk0 + 4 * c4 + j);
     }
     if (a.qk_l2norm) {
       const float nk = group_sum<LPR>(kk[0] * kk[0] + kk[1] * kk[1] + kk[2] * kk[2] + kk[3] * kk[3]);
-      const float nq = group_sum<LPR>(qq[0] * qq[0] + qq[1] * qq[1] + qq[2] * qq[2] + qq[3] * qq[3]);
-      const float rk = 1.f / sqrtf(nk + 1e-6f), rq = 1.f / sqrtf(nq + 1e-6f);
+      const float rk = 1.f / sqrtf(nk + 1e-6f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kk[j] *= rk;
-        qq[j] *= rq;
+      for (int j = 0; j < 4; ++j) kk[j] *= rk;
+      if constexpr (OUT) {
+        const float nq = group_sum<LPR>(qq[0] * qq[0] + qq[1] * qq[1] + qq[2] * qq[2] + qq[3] * qq[3]);
+        const float rq = 1.f / sqrtf(nq + 1e-6f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qq[j] *= rq;
       }
     }
     float b = ld_in(beta, g0), dec = 1.f;
@@ -252,22 +255,35 @@ __global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
       dec = expf(g);
     }
 
-    float vals[2 * RPT];
+    if constexpr (OUT) {
+      float vals[2 * RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      vals[2 * i] = st[i][0] * kk[0] + st[i][1] * kk[1] + st[i][2] * kk[2] + st[i][3] * kk[3];
-      vals[2 * i + 1] = st[i][0] * qq[0] + st[i][1] * qq[1] + st[i][2] * qq[2] + st[i][3] * qq[3];
-    }
-    const float kq = group_sum<LPR>(kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3]);
-    reduce_scatter<LPR>(vals, c4);
-    const int row = rg + RG * (c4 >> 1);
-    const float r_or_p = vals[0];
-    const float u = b * (ld_in(v, (tok * a.H + h) * D + row) - dec * r_or_p);
-    const float u_even = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(u), 0xA0, 0xf, 0xf, false));
-    if (c4 & 1) {
-      if (o) st_out(o, (tok * a.H + h) * D + row, dec * r_or_p + u_even * kq);
+      for (int i = 0; i < RPT; ++i) {
+        vals[2 * i] = st[i][0] * kk[0] + st[i][1] * kk[1] + st[i][2] * kk[2] + st[i][3] * kk[3];
+        vals[2 * i + 1] = st[i][0] * qq[0] + st[i][1] * qq[1] + st[i][2] * qq[2] + st[i][3] * qq[3];
+      }
+      const float kq = group_sum<LPR>(kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3]);
+      reduce_scatter<LPR>(vals, c4);
+      const int row = rg + RG * (c4 >> 1);
+      const float r_or_p = vals[0];
+      const float u = b * (ld_in(v, (tok * a.H + h) * D + row) - dec * r_or_p);
+      const float u_even = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(u), 0xA0, 0xf, 0xf, false));
+      if (c4 & 1) {
+        st_out(o, (tok * a.H + h) * D + row, dec * r_or_p + u_even * kq);
+      } else {
+        ush[lane_slot][row] = u;
+      }
     } else {
-      ush[lane_slot][row] = u;
+      // RPT key products over the row's LPR = 2 RPT lanes: reduce-scatter inside each half,
+      // then add the other half's partial sums; lanes c4 and c4 + RPT hold row value c4 mod RPT
+      float vals[RPT];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        vals[i] = st[i][0] * kk[0] + st[i][1] * kk[1] + st[i][2] * kk[2] + st[i][3] * kk[3];
+      reduce_scatter<RPT>(vals, c4);
+      const float r = vals[0] + xor_lane<RPT>(vals[0]);
+      const int row = rg + RG * (c4 & (RPT - 1));
+      if (c4 < RPT) ush[lane_slot][row] = b * (ld_in(v, (tok * a.H + h) * D + row) - dec * r);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -500,12 +516,14 @@ hipError_t launch_decode_ex_t(const DecodeExArgs& a, hipStream_t stream) {
       return hipGetLastError();
     }
   }
-  if (a.kda)
-    hipLaunchKernelGGL((decode_ex_kernel<D, TIn, TOut, true>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((decode_ex_kernel<D, TIn, TOut, false>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       stream, a);
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (a.kda) {
+    if (a.o) hipLaunchKernelGGL((decode_ex_kernel<D, TIn, TOut, true, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((decode_ex_kernel<D, TIn, TOut, true, false>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (a.o) hipLaunchKernelGGL((decode_ex_kernel<D, TIn, TOut, false, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((decode_ex_kernel<D, TIn, TOut, false, false>), grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

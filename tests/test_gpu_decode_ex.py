@@ -35,7 +35,7 @@ def _live(inp):
     return np.nonzero((s >= 0) & (s < inp["pool"].shape[0]))[0]
 
 
-@pytest.mark.parametrize("D", [16, 64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("kda,raw", [(False, False), (True, False), (False, True)])
 def test_window_verify_then_commit(D, dtype, kda, raw):
