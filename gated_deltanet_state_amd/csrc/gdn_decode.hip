@@ -85,6 +85,42 @@ __device__ __forceinline__ void reduce_scatter(float* vals, int lane) {
 
 constexpr int kThreads = 256;
 typedef float f4v __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// The state rows one lane touches: float4 number lane_f4 + off of the state.  When a state's
+// lanes fill whole wavefronts the base is the same in every lane, so the rows go through a
+// buffer descriptor: one lane offset in a register, each row's offset a scalar constant,
+// instead of one 64-bit address per row.  Loads are ordinary; stores are non-temporal (the
+// descriptor's nt cache-policy bit).
+template <int D, bool UNIFORM>
+struct StateRows;
+template <int D>
+struct StateRows<D, true> {
+  __amdgpu_buffer_rsrc_t r;
+  int voff;
+  __device__ __forceinline__ StateRows(float* base, int lane_f4) : voff(16 * lane_f4) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t u = static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b)))) |
+                       static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32)))) << 32;
+    r = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), 0, D * D * 4, 0x00020000);
+  }
+  __device__ __forceinline__ f4v load(int off) const {
+    return __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 16 * off, 0));
+  }
+  // the store takes its row offset in the lane offset and a zero scalar offset: a store of
+  // more than 8 bytes with a register scalar offset is exempt from the compiler's wait state
+  // before its data registers are overwritten
+  __device__ __forceinline__ void store(int off, f4v x) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), r, voff + 16 * off, 0, 2);
+  }
+};
+template <int D>
+struct StateRows<D, false> {
+  f4v* p;
+  __device__ __forceinline__ StateRows(float* base, int lane_f4) : p(reinterpret_cast<f4v*>(base) + lane_f4) {}
+  __device__ __forceinline__ f4v load(int off) const { return p[off]; }
+  __device__ __forceinline__ void store(int off, f4v x) const { __builtin_nontemporal_store(x, p + off); }
+};
 
 template <int D, typename TIn, typename TOut>
 __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ state,
@@ -114,10 +150,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ st
   // the states stream through once per step. Ordinary loads (the non-temporal hint on the
   // loads measured about 12% slower for the same bytes); the stores stay non-temporal (plain
   // stores measured about 25% slower)
-  f4v* S = reinterpret_cast<f4v*>(state + s * D * D);
+  // (the descriptor form of the serving kernel below lifts this kernel to 5 waves per SIMD
+  // but measured the same, so it keeps one address per row)
+  StateRows<D, false> S(state + s * D * D, rg * LPR + c4);
   f4v st[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) st[i] = S[(rg + RG * i) * LPR + c4];
+  for (int i = 0; i < RPT; ++i) st[i] = S.load(i * RG * LPR);
 
   float kk[4], qq[4];
 #pragma unroll
@@ -156,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ st
     f4v x = st[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) x[j] = a * x[j] + ui * kk[j];
-    __builtin_nontemporal_store(x, &S[(rg + RG * i) * LPR + c4]);
+    S.store(i * RG * LPR, x);
   }
 }
 
@@ -178,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(float* __restrict__ st
 // last committed token is stored as soon as it exists.  Without outputs (OUT false: commit
 // alone) only the key products S k are formed and reduced.
 template <int D, typename TIn, typename TOut, bool KDA, bool OUT>
-__global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void decode_ex_kernel(DecodeExArgs a) {
   constexpr int LPR = D / 4, RG = 8, TPS = LPR * RG, SPB = kThreads / TPS, RPT = D / RG;
   static_assert(2 * RPT == LPR, "one reduced value per lane");
   __shared__ float ush[SPB][D];
@@ -206,10 +244,10 @@ __global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
   if (tend == 0) return;
 
   const int lt = tid % TPS, c4 = lt % LPR, rg = lt / LPR;
-  f4v* S = reinterpret_cast<f4v*>(a.pool + (row_slot * a.H + h) * D * D);
+  StateRows<D, (TPS >= 64)> S(a.pool + (row_slot * a.H + h) * D * D, rg * LPR + c4);
   f4v st[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) st[i] = S[(rg + RG * i) * LPR + c4];
+  for (int i = 0; i < RPT; ++i) st[i] = S.load(i * RG * LPR);
   float A = 0.f, dtb = 0.f;
   if (!KDA && a.raw_gates) {
     A = __expf(a.A_log[h]);
@@ -300,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void decode_ex_kernel(DecodeExArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (t + 1 == ncommit) {
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) __builtin_nontemporal_store(st[i], &S[(rg + RG * i) * LPR + c4]);
+      for (int i = 0; i < RPT; ++i) S.store(i * RG * LPR, st[i]);
     }
   }
 }
