@@ -254,6 +254,12 @@ __global__ __launch_bounds__(kThreads, 4) void decode_ex_kernel(DecodeExArgs a) 
     dtb = a.dt_bias[h];
   }
 
+  // Commit (no outputs) keeps the state as S = cs S' with a running scale cs, the product of
+  // the scalar decays so far: a token adds (u / cs) k^T to S' with one FMA per element, and
+  // S' is multiplied by cs once, when stored.  If cs would fall below 2^-60 it is first
+  // folded into the rows and that token takes the direct update, so 1 / cs stays finite.
+  // (KDA has no scalar decay here, so cs stays 1.)
+  float cs = 1.f;
   for (int t = 0; t < tend; ++t) {
     const int64_t tok = n * a.T + t;
     const int64_t qk0 = (tok * a.Hqk + hq) * D, g0 = tok * a.H + h;
@@ -292,6 +298,20 @@ __global__ __launch_bounds__(kThreads, 4) void decode_ex_kernel(DecodeExArgs a) 
       }
       dec = expf(g);
     }
+    bool lazy = false;
+    float rc = 1.f;
+    if constexpr (!OUT) {
+      const float cn = cs * dec;
+      lazy = cn >= 0x1p-60f;
+      if (lazy) {
+        rc = 1.f / cn;
+        cs = cn;
+      } else {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) st[i] *= cs;
+        cs = 1.f;
+      }
+    }
 
     if constexpr (OUT) {
       float vals[2 * RPT];
@@ -321,16 +341,27 @@ __global__ __launch_bounds__(kThreads, 4) void decode_ex_kernel(DecodeExArgs a) 
       reduce_scatter<RPT>(vals, c4);
       const float r = vals[0] + xor_lane<RPT>(vals[0]);
       const int row = rg + RG * (c4 & (RPT - 1));
-      if (c4 < RPT) ush[lane_slot][row] = b * (ld_in(v, (tok * a.H + h) * D + row) - dec * r);
+      // lazy: r is S'_{t-1} k and the stored correction is u / cs = beta (v / cs - r)
+      const float vr = ld_in(v, (tok * a.H + h) * D + row);
+      if (c4 < RPT) ush[lane_slot][row] = lazy ? b * (vr * rc - r) : b * (vr - dec * r);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lazy) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const float ui = ush[lane_slot][rg + RG * i];
+      for (int i = 0; i < RPT; ++i) {
+        const float ui = ush[lane_slot][rg + RG * i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st[i][j] = dec * st[i][j] + ui * kk[j];
+        for (int j = 0; j < 4; ++j) st[i][j] += ui * kk[j];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float ui = ush[lane_slot][rg + RG * i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st[i][j] = dec * st[i][j] + ui * kk[j];
+      }
     }
     // the next token overwrites the corrections only after every lane has read them
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -338,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_ex_kernel(DecodeExArgs a) 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (t + 1 == ncommit) {
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) S.store(i * RG * LPR, st[i]);
+      for (int i = 0; i < RPT; ++i) S.store(i * RG * LPR, OUT ? st[i] : st[i] * cs);
     }
   }
 }

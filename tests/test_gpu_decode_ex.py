@@ -213,3 +213,32 @@ def test_verify_misaligned_qk_views(dtype):
     tol = 1e-5 if dtype == torch.float32 else 2e-3
     assert rel_l2(o_m, o_ref) <= tol and rel_l2(o_a, o_ref) <= tol
     assert rel_l2(o_m, o_a) <= 1e-5
+
+
+@pytest.mark.parametrize("D", [16, 128])
+def test_commit_strong_decay_against_oracle(D):
+    """Commit keeps the state as a running scale times rows and folds the scale in once the
+    decays' product would fall below 2^-60.  Gates that cross that point at different tokens
+    (log alpha -15 per token folds at the third; -50 folds at once; -30/-2 alternate; -0.01
+    never folds), every token committed, fp32 inputs: pool rows against the oracle."""
+    import gated_deltanet_state_amd as g
+    N, T, H, Hqk, P = 5, 6, 4, 2, 9
+    say(f"commit strong decay D={D}")
+    inp = synth.make_serving(N, T, H, Hqk, D, P, torch.float32, seed=71 + D)
+    la = torch.empty(N, T, H)
+    la[0] = -15.0
+    la[1] = -0.05
+    la[1, 0] = -50.0
+    la[2, 0::2], la[2, 1::2] = -30.0, -2.0
+    la[3] = -0.01
+    la[4] = torch.linspace(-40.0, -1.0, T).view(T, 1)
+    inp["log_alpha"] = la
+    inp["n_commit"] = torch.full((N,), T, dtype=torch.int32)
+    d = _cuda(inp)
+    g.gdn_decode_commit(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["n_commit"],
+                        slots=d["slots"])
+    torch.cuda.synchronize()
+    _, pool_ref = _ref(inp, kda=False, raw=False, write_state=True)
+    used = inp["slots"].numpy()[_live(inp)]
+    for r in used:
+        assert rel_l2(d["pool"][int(r)], pool_ref[int(r)]) <= 1e-5, r
