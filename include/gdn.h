@@ -238,6 +238,9 @@ gdn_status_t gdn_decode_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv, gdn_d
  * that only verifies (write_state = 0, o given) with kda = 0, Dk = 128, T <= 8 and q, k
  * aligned to 4 elements is computed as one chunk of the chunkwise form on the fp32 matrix
  * cores; its outputs agree with the token-by-token result to fp32 rounding, not bit for bit.
+ * A commit without outputs (write_state = 1, o = NULL, scalar gate) carries the product of
+ * the decays as a running scale applied once at the store; the committed rows agree with
+ * the token-by-token result to fp32 rounding, not bit for bit.
  * Supported:
  * Dk == Dv in {16, 32, 64, 128}; raw_gates with kda is NOT_SUPPORTED.  Two sequences
  * must not share a slot in one call (their writes would race).  N = 0, or o = NULL with
