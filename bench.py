@@ -115,7 +115,7 @@ def main():
                     help="run a subset (for profiling); the JSON line needs 'all' or 'prefill'")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the (batch, head) streams shard with no exchange, see the design notes)", file=sys.stderr)
         sys.exit(2)
 
