@@ -215,15 +215,16 @@ def test_verify_misaligned_qk_views(dtype):
     assert rel_l2(o_m, o_a) <= 1e-5
 
 
-@pytest.mark.parametrize("D", [16, 128])
-def test_commit_strong_decay_against_oracle(D):
+@pytest.mark.parametrize("D,T", [(16, 6), (128, 6), (128, 33)])
+def test_commit_strong_decay_against_oracle(D, T):
     """Commit keeps the state as a running scale times rows and folds the scale in once the
     decays' product would fall below 2^-60.  Gates that cross that point at different tokens
     (log alpha -15 per token folds at the third; -50 folds at once; -30/-2 alternate; -0.01
-    never folds), every token committed, fp32 inputs: pool rows against the oracle."""
+    never folds), every token committed, fp32 inputs: pool rows against the oracle.  A window
+    of 33 tokens folds many times along the way."""
     import gated_deltanet_state_amd as g
-    N, T, H, Hqk, P = 5, 6, 4, 2, 9
-    say(f"commit strong decay D={D}")
+    N, H, Hqk, P = 5, 4, 2, 9
+    say(f"commit strong decay D={D} T={T}")
     inp = synth.make_serving(N, T, H, Hqk, D, P, torch.float32, seed=71 + D)
     la = torch.empty(N, T, H)
     la[0] = -15.0
