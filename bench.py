@@ -83,9 +83,23 @@ def time_launches(fn, steps: int, warmup: int, torch) -> float:
     return s.elapsed_time(e) / steps
 
 
-def cpu_baseline_prefill(inp, min_seconds: float = 10.0, max_reps: int = 200):
+def cpu_model() -> str:
+    """The host CPU's model name, as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline_prefill(inp, min_seconds: float = 8.0, max_reps: int = 200, single_seconds: float = 2.0):
     """The fp64 oracle, as it stands, on the whole workload (every (batch, head) stream, all
-    tokens) on all host cores, repeated until at least `min_seconds` of wall time."""
+    tokens) on all host cores, repeated until at least `min_seconds` of wall time; then on one
+    thread over the first two streams, repeated until `single_seconds`."""
     import oracle
     oracle.build(force=False)
     B, H, T, d = inp["q"].shape
@@ -99,9 +113,48 @@ def cpu_baseline_prefill(inp, min_seconds: float = 10.0, max_reps: int = 200):
         if dt >= min_seconds or reps >= max_reps:
             break
     tokens = reps * B * T  # a token carries all H heads
+    # one thread, two (batch, head) streams: head-tokens per second, scaled to tokens of H heads
+    sub = tuple(None if x is None else x[:1, :2].contiguous() for x in args)
+    reps1 = 0
+    t1 = time.perf_counter()
+    while True:
+        oracle.forward(*sub, nthreads=1)
+        reps1 += 1
+        dt1 = time.perf_counter() - t1
+        if dt1 >= single_seconds or reps1 >= max_reps:
+            break
+    head_tok_s1 = reps1 * 2 * T / dt1
     return {"value": round(tokens / dt / 1e6, 6), "unit": "Mtok/s", "cores": int(threads), "kind": "oracle",
             "sample": f"whole workload ({B * H} streams x {T} tokens) repeated {reps} times, fp64 token "
-                      f"loop, {dt:.1f} s wall"}
+                      f"loop, {dt:.1f} s wall",
+            "cpu": cpu_model(),
+            "single_thread": {"value": round(head_tok_s1 / H / 1e6, 6), "unit": "Mtok/s", "cores": 1,
+                              "sample": f"2 streams x {T} tokens on one thread, repeated {reps1} times, "
+                                        f"{dt1:.1f} s wall; scaled to tokens of {H} heads"}}
+
+
+def cpu_baseline_decode(inp, min_seconds: float = 3.0, max_steps: int = 100):
+    """The fp64 oracle's decode step on every (sequence, head) state of the decode workload, on
+    all host cores, stepping until `min_seconds` of wall time.  State traffic is counted in
+    the oracle's own fp64 bytes (read and write once per step)."""
+    import oracle
+    oracle.build(force=False)
+    st = inp["state"].double().numpy().copy()
+    N, H, Dv, Dk = st.shape
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        t = steps % inp["q"].shape[0]
+        oracle.decode_step(st, *(inp[k][t] for k in ("q", "k", "v", "beta", "log_alpha")))
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or steps >= max_steps:
+            break
+    fp64_bytes = 2 * N * H * Dv * Dk * 8
+    return {"value": round(steps * fp64_bytes / dt / 1e9, 3), "unit": "GB/s (fp64 state)",
+            "cores": int(oracle.hardware_threads()), "kind": "oracle",
+            "us_per_step": round(dt / steps * 1e6, 1),
+            "sample": f"{steps} steps over all {N * H} states of {Dv}x{Dk}, {dt:.1f} s wall"}
 
 
 def main():
@@ -215,6 +268,11 @@ def main():
                          "kernel": "decode_kernel", "algorithmic_bytes": state_bytes + io_bytes},
         }
         log(f"decode: {per*1e3:.1f} us/step, state {gbs:.0f} GB/s, HBM frac {hbm/HBM_PEAK_GBS:.3f}")
+        if not args.no_cpu_baseline and args.only == "all":
+            log("cpu baseline: fp64 oracle decode step on the host cores")
+            cpu_dec = cpu_baseline_decode(inp)
+            if "cpu_baseline" in out:
+                out["cpu_baseline"]["decode"] = cpu_dec
         del st, dq, inp
         torch.cuda.empty_cache()
 

@@ -3,7 +3,7 @@
 The functions here carry the names of the C ABI in ``include/gdn.h`` and only
 marshal arguments: they check shapes, dtypes and devices, allocate outputs through
 PyTorch when the caller does not pass them, and hand raw device pointers and the
-current HIP stream to the library.  Every step of the computation runs in the HIP
+HIP stream (the caller's, or torch's current one) to the library.  Every step of the computation runs in the HIP
 kernels; there is no fallback.  If ``libgdn.so`` is missing, importing this package
 fails loudly.
 """
@@ -67,8 +67,9 @@ class GdnError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(library_path):
         raise ImportError(
-            f"{library_path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
-            "(hipcc --offload-arch=gfx950). There is no CPU fallback.")
+            f"{library_path} is not built; build it with `python gated_deltanet_state_amd/build.py` "
+            "(hipcc --offload-arch=gfx950; `__graft_entry__.build()` does the same and also builds the "
+            "test oracle). There is no CPU fallback.")
     L = ctypes.CDLL(library_path)
     vp, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     dp = ctypes.POINTER(GdnChunkDesc)
@@ -115,22 +116,46 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    if isinstance(stream, torch.cuda.Stream):
-        return ctypes.c_void_p(stream.cuda_stream)
-    return ctypes.c_void_p(int(stream))
+class _Launch:
+    """The stream a call runs on, and the tensors the binding allocated for it.
+
+    Work is enqueued on ``stream`` (default: torch's current stream).  Tensors that the
+    binding allocates come from torch's caching allocator on the current stream; when the
+    kernels run on another stream, each such tensor is marked as used by that stream
+    (``record_stream``), so that its memory is not handed to new work on the current stream
+    while the kernels may still read or write it."""
+
+    def __init__(self, stream):
+        cur = torch.cuda.current_stream()
+        if stream is None:
+            stream = cur
+        elif not isinstance(stream, torch.cuda.Stream):
+            stream = torch.cuda.ExternalStream(int(stream))
+        self.stream = stream
+        self.handle = ctypes.c_void_p(stream.cuda_stream)
+        self.other = stream.cuda_stream != cur.cuda_stream
+        self.owned = []
+
+    def new(self, *shape, **kw) -> torch.Tensor:
+        t = torch.empty(*shape, **kw)
+        self.owned.append(t)
+        return t
+
+    def done(self) -> None:
+        if self.other:
+            for t in self.owned:
+                if t.is_cuda:
+                    t.record_stream(self.stream)
 
 
-def _ckpt_buffer(s_ckpt, shape, device, to_host: bool):
+def _ckpt_buffer(L: "_Launch", s_ckpt, shape, device, to_host: bool):
     """The snapshot buffer: on the device, or in pinned host memory (written by the kernel
     directly, see s_ckpt in include/gdn.h) when ``to_host`` or when a pinned CPU tensor is
     passed."""
     if s_ckpt is None:
         if to_host:
             return torch.empty(shape, dtype=torch.float32, pin_memory=True)
-        return torch.empty(shape, dtype=torch.float32, device=device)
+        return L.new(shape, dtype=torch.float32, device=device)
     if s_ckpt.device.type == "cpu":
         if not s_ckpt.is_pinned():
             raise ValueError("s_ckpt on the host must be pinned memory (pin_memory=True)")
@@ -177,6 +202,7 @@ def _chunk_fwd(kda: bool, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_d
     dev, in_dt = q.device, q.dtype
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    L = _Launch(stream)
     out_dt = out_dtype or in_dt
     _check(k, "k", (B, H, T, D), in_dt, dev)
     _check(v, "v", (B, H, T, D), in_dt, dev)
@@ -186,14 +212,14 @@ def _chunk_fwd(kda: bool, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_d
     if s0 is not None:
         _check(s0, "s0", (B, H, D, D), torch.float32, dev)
     if o is None:
-        o = torch.empty(B, H, T, D, dtype=out_dt, device=dev)
+        o = L.new(B, H, T, D, dtype=out_dt, device=dev)
     _check(o, "o", (B, H, T, D), out_dt, dev)
     if s_final is None and return_final:
-        s_final = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+        s_final = L.new(B, H, D, D, dtype=torch.float32, device=dev)
     if s_final is not None:
         _check(s_final, "s_final", (B, H, D, D), torch.float32, dev)
     n_ck = T // ckpt_every if ckpt_every > 0 else 0
-    s_ckpt = _ckpt_buffer(s_ckpt, (B, H, n_ck, D, D), dev, snapshots_to_host) if n_ck > 0 else None
+    s_ckpt = _ckpt_buffer(L, s_ckpt, (B, H, n_ck, D, D), dev, snapshots_to_host) if n_ck > 0 else None
     d = _desc(B, H, T, D, chunk, in_dt, out_dt, ckpt_every)
     fn = lib.kda_chunk_fwd if kda else lib.gdn_chunk_fwd
     # the matrix-core KDA prefill runs in its two-kernel form when given its workspace
@@ -205,12 +231,13 @@ def _chunk_fwd(kda: bool, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_d
             raise GdnError(st, "gdn_chunk_workspace_size")
         if need.value > 0:
             if workspace is None:
-                workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+                workspace = L.new(need.value, dtype=torch.uint8, device=dev)
             ws, ws_bytes = workspace, workspace.numel() * workspace.element_size()
     st = fn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(s0),
-            _ptr(o), _ptr(s_final), _ptr(s_ckpt), _ptr(ws), ws_bytes, _stream(stream))
+            _ptr(o), _ptr(s_final), _ptr(s_ckpt), _ptr(ws), ws_bytes, L.handle)
     if st != GDN_SUCCESS:
         raise GdnError(st, "kda_chunk_fwd" if kda else "gdn_chunk_fwd")
+    L.done()
     return o, s_final, s_ckpt
 
 
@@ -251,18 +278,20 @@ def gdn_decode_step(state, q, k, v, beta, log_alpha, *, o=None, out_dtype=None, 
     dev, in_dt = q.device, q.dtype
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    L = _Launch(stream)
     _check(state, "state", (N, H, D, D2), torch.float32, dev)
     for name, t, shp in (("q", q, (N, H, D2)), ("k", k, (N, H, D2)), ("v", v, (N, H, D)),
                          ("beta", beta, (N, H)), ("log_alpha", log_alpha, (N, H))):
         _check(t, name, shp, in_dt, dev)
     out_dt = out_dtype or in_dt
     if o is None:
-        o = torch.empty(N, H, D, dtype=out_dt, device=dev)
+        o = L.new(N, H, D, dtype=out_dt, device=dev)
     _check(o, "o", (N, H, D), out_dt, dev)
     st = lib.gdn_decode_step(N, H, D2, D, _code(in_dt), _code(out_dt), _ptr(state), _ptr(q), _ptr(k),
-                             _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(o), _stream(stream))
+                             _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(o), L.handle)
     if st != GDN_SUCCESS:
         raise GdnError(st, "gdn_decode_step")
+    L.done()
     return o
 
 
@@ -283,6 +312,7 @@ def gdn_decode_ex(pool, q, k, v, beta, log_alpha, *, slots=None, n_commit=None, 
     dev, in_dt = q.device, q.dtype
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    L = _Launch(stream)
     _check(pool, "pool", (P, H, D, D), torch.float32, dev)
     for name, t, shp in (("k", k, (N, T, Hqk, D)), ("v", v, (N, T, H, D)), ("beta", beta, (N, T, H)),
                          ("log_alpha", log_alpha, (N, T, H, D) if kda else (N, T, H))):
@@ -296,15 +326,16 @@ def gdn_decode_ex(pool, q, k, v, beta, log_alpha, *, slots=None, n_commit=None, 
             _check(t, name, (N,), torch.int32, dev)
     out_dt = out_dtype or in_dt
     if o is None and return_o:
-        o = torch.empty(N, T, H, D, dtype=out_dt, device=dev)
+        o = L.new(N, T, H, D, dtype=out_dt, device=dev)
     if o is not None:
         _check(o, "o", (N, T, H, D), out_dt, dev)
     d = GdnDecodeExDesc(N, H, Hqk, D, D, T, P, _code(in_dt), _code(out_dt), int(kda), int(qk_l2norm),
                         int(raw), int(write_state))
     st = lib.gdn_decode_ex(ctypes.byref(d), _ptr(pool), _ptr(slots), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
-                           _ptr(log_alpha), _ptr(A_log), _ptr(dt_bias), _ptr(n_commit), _ptr(o), _stream(stream))
+                           _ptr(log_alpha), _ptr(A_log), _ptr(dt_bias), _ptr(n_commit), _ptr(o), L.handle)
     if st != GDN_SUCCESS:
         raise GdnError(st, "gdn_decode_ex")
+    L.done()
     return o
 
 
@@ -336,6 +367,7 @@ def gdn_chunk_fwd_ex(q, k, v, beta, log_alpha, s0=None, *, A_log=None, dt_bias=N
     dev, in_dt = q.device, q.dtype
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    L = _Launch(stream)
     out_dt = out_dtype or in_dt
     _check(k, "k", (B, Hqk, T, D), in_dt, dev)
     _check(v, "v", (B, H, T, D), in_dt, dev)
@@ -348,20 +380,21 @@ def gdn_chunk_fwd_ex(q, k, v, beta, log_alpha, s0=None, *, A_log=None, dt_bias=N
     if s0 is not None:
         _check(s0, "s0", (B, H, D, D), torch.float32, dev)
     if o is None:
-        o = torch.empty(B, H, T, D, dtype=out_dt, device=dev)
+        o = L.new(B, H, T, D, dtype=out_dt, device=dev)
     _check(o, "o", (B, H, T, D), out_dt, dev)
     if s_final is None and return_final:
-        s_final = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+        s_final = L.new(B, H, D, D, dtype=torch.float32, device=dev)
     if s_final is not None:
         _check(s_final, "s_final", (B, H, D, D), torch.float32, dev)
     n_ck = T // ckpt_every if ckpt_every > 0 else 0
-    s_ckpt = _ckpt_buffer(s_ckpt, (B, H, n_ck, D, D), dev, snapshots_to_host) if n_ck > 0 else None
+    s_ckpt = _ckpt_buffer(L, s_ckpt, (B, H, n_ck, D, D), dev, snapshots_to_host) if n_ck > 0 else None
     d = GdnChunkExDesc(_desc(B, H, T, D, chunk, in_dt, out_dt, ckpt_every), Hqk, int(raw), int(bool(qk_l2norm)))
     st = lib.gdn_chunk_fwd_ex(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
                               _ptr(A_log), _ptr(dt_bias), None, _ptr(s0), _ptr(o), _ptr(s_final), _ptr(s_ckpt),
-                              _stream(stream))
+                              L.handle)
     if st != GDN_SUCCESS:
         raise GdnError(st, "gdn_chunk_fwd_ex")
+    L.done()
     return o, s_final, s_ckpt
 
 
@@ -403,6 +436,7 @@ def gdn_chunk_fwd_ragged(q, k, v, beta, log_alpha, cu_seqlens, *, H: int, H_qk: 
     dev, in_dt = q.device, q.dtype
     if dev.type != "cuda":
         raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    L = _Launch(stream)
     out_dt = out_dtype or in_dt
     _check(k, "k", (H_qk * T, D), in_dt, dev)
     _check(v, "v", (H * T, D), in_dt, dev)
@@ -416,16 +450,17 @@ def gdn_chunk_fwd_ragged(q, k, v, beta, log_alpha, cu_seqlens, *, H: int, H_qk: 
     if s0 is not None:
         _check(s0, "s0", (B, H, D, D), torch.float32, dev)
     if o is None:
-        o = torch.empty(H * T, D, dtype=out_dt, device=dev)
+        o = L.new(H * T, D, dtype=out_dt, device=dev)
     _check(o, "o", (H * T, D), out_dt, dev)
     if s_final is None and return_final:
-        s_final = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+        s_final = L.new(B, H, D, D, dtype=torch.float32, device=dev)
     if s_final is not None:
         _check(s_final, "s_final", (B, H, D, D), torch.float32, dev)
     d = GdnChunkExDesc(_desc(B, H, T, D, 64, in_dt, out_dt, 0), H_qk, int(raw), int(bool(qk_l2norm)))
     st = lib.gdn_chunk_fwd_ex(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
                               _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens), _ptr(s0), _ptr(o), _ptr(s_final),
-                              None, _stream(stream))
+                              None, L.handle)
     if st != GDN_SUCCESS:
         raise GdnError(st, "gdn_chunk_fwd_ex")
+    L.done()
     return o, s_final

@@ -1,8 +1,10 @@
 // gdn_api.cpp -- the extern "C" entry points of libgdn.so: synchronous host-side
 // validation, then dispatch to one kernel launch on the caller's stream.
 //
-// Nothing here touches device memory or synchronises; every check runs before the
-// first HIP call, so a rejected call has launched nothing.
+// Nothing here touches device memory or synchronises.  The only HIP call made during
+// validation is the pointer-attribute query on a snapshot buffer (is it device memory or
+// pinned host memory?); every check, that one included, runs before any launch, so a
+// rejected call has launched nothing.
 #include <stdint.h>
 #include <string.h>
 
@@ -17,7 +19,14 @@ bool aligned_elem(const void* p, gdn_dtype_t dt) {
   return (reinterpret_cast<uintptr_t>(p) & m) == 0;
 }
 
-bool valid_dtype(gdn_dtype_t d) { return d == GDN_F32 || d == GDN_BF16; }
+// A dtype field or argument is checked through its integer bits: a caller can pass any int,
+// and reading an out-of-range value as the enum type is undefined behaviour in C++.
+bool valid_dtype(const gdn_dtype_t& d) {
+  int v;
+  memcpy(&v, &d, sizeof v);
+  return v == GDN_F32 || v == GDN_BF16;
+}
+static_assert(sizeof(gdn_dtype_t) == sizeof(int), "gdn_dtype_t is an int");
 
 // Byte ranges [a, a + na) and [b, b + nb) intersect.
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -123,17 +132,18 @@ gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, con
     if (!s_ckpt || !aligned16(s_ckpt)) return GDN_ERROR_INVALID_VALUE;
     // Snapshots may go to pinned host memory: the kernel then writes each one into host RAM
     // as it is reached, with no copy and no synchronisation.  Pageable host memory, which the
-    // GPU cannot write, is rejected; a pointer the runtime does not know is taken as device
-    // memory, as for every other argument.
+    // GPU cannot write, is rejected, and so is a pointer the runtime cannot describe: storing
+    // through it could fault the GPU.
     hipPointerAttribute_t at;
-    if (hipPointerGetAttributes(&at, s_ckpt) == hipSuccess) {
-      if (at.type == hipMemoryTypeUnregistered) return GDN_ERROR_INVALID_VALUE;
-      if (at.type == hipMemoryTypeHost) {
-        if (!at.devicePointer || !aligned16(at.devicePointer)) return GDN_ERROR_INVALID_VALUE;
-        s_ckpt = static_cast<float*>(at.devicePointer);
-      }
-    } else {
-      (void)hipGetLastError();  // the failed query must not be reported by the launch
+    if (hipPointerGetAttributes(&at, s_ckpt) != hipSuccess) {
+      (void)hipGetLastError();  // the failed query must not be reported by a later call
+      return GDN_ERROR_INVALID_VALUE;
+    }
+    if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged && at.type != hipMemoryTypeHost)
+      return GDN_ERROR_INVALID_VALUE;
+    if (at.type == hipMemoryTypeHost) {
+      if (!at.devicePointer || !aligned16(at.devicePointer)) return GDN_ERROR_INVALID_VALUE;
+      s_ckpt = static_cast<float*>(at.devicePointer);
     }
   } else {
     s_ckpt = nullptr;

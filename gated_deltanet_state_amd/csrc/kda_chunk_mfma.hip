@@ -16,9 +16,15 @@
 //   * off the diagonal 16-token blocks (j in block J < R = block of r) the split point is the
 //     end of block J: (k_r e^{G_r - G_end(J)}) . (k_j e^{G_end(J) - G_j}), both factors <= 1
 //     for any gate strength;
-//   * inside a diagonal block the split point is its middle token m: factors are bounded by
-//     e^{8 max|log alpha|}, which stays in half range while the log-gates of 8 consecutive
-//     tokens sum to more than -11 in every channel (documented precondition of this path).
+//   * inside a diagonal block the split point is its middle token m, with factors up to
+//     e^{G_start - G_m} and e^{G_m - G_end} per channel.  While both stay below e^8 (and the
+//     rows times the factors stay in half range) the block runs on the matrix cores like the
+//     others.  A block whose gates are stronger is flagged when its chunk is staged: its rows
+//     take the block start as their reference instead (all their factors <= 1), and its two
+//     diagonal 16x16 tiles of A and P are formed exactly in fp32, each factor
+//     e^{G_r - G_j} <= 1 computed for its own pair (r, j) and channel.  So every finite gate
+//     <= 0 gives finite, accurate results; strong gates only cost the flagged blocks' extra
+//     work.
 // Work decomposition as in the scalar-gate kernel (a workgroup per stream and 32 value rows,
 // 8 wavefronts), without its cross-chunk pipelining: the per-channel operand tiles fill the
 // LDS.  Per chunk: stage (log-gate prefix per channel, scaled operand tiles) | Gram/score
@@ -48,12 +54,26 @@ constexpr int LC = C + 8;    // row stride (halves) of [channel][token] and [tok
 constexpr int LT = 24;       // row stride (halves) of 16x16 blocks
 constexpr int LG = D + 4;    // row stride (floats) of the fp32 prefix G[token][channel]
 
+// Reference point of the rows of block R: its middle token m(R) = 16 R + 7, or for a flagged
+// block (strong gates, see DiagFlags) the state entering it, G_ref = G_{16R-1} (0 for R = 0).
 struct alignas(16) Tables {
   alignas(16) float beta[C];
-  alignas(16) float em[4][D];     // e^{G_m(R)}, m(R) = 16 R + 7: turns k e^{G - G_m} into k e^{G}
-  alignas(16) float fm[4][4][D];  // fm[R][J] = e^{G_m(R) - G_end(J)}, J < R, G_end(J) = G_{16J+15}
+  alignas(16) float em[4][D];     // e^{G_ref(R)}: turns k e^{G - G_ref} into k e^{G}
+  alignas(16) float fm[4][4][D];  // fm[R][J] = e^{G_ref(R) - G_end(J)} <= 1, J < R, G_end(J) = G_{16J+15}
   alignas(16) float gc[D];        // e^{G_63}
 };
+
+// Blocks whose diagonal tiles are formed exactly (bit R), and the largest |q|, |k| element of
+// each block's rows (one entry per staging wavefront: keys 0..3, queries 4..7).
+struct alignas(16) DiagFlags {
+  float rowmax[8];
+  int bits;
+};
+// A block runs its diagonal tiles on the matrix cores while both middle-token factors stay
+// below e^kDiagExp (so the small ones stay normal halves) and rows times factors below
+// kDiagLimit (half range with margin).
+constexpr float kDiagExp = 8.f;
+constexpr float kDiagLimit = 16384.f;
 
 struct alignas(16) Products {
   alignas(16) _Float16 p[C][LC];        // tril((Q*Gamma)(K/Gamma)^T), inclusive
@@ -81,6 +101,8 @@ struct alignas(16) Smem {
     Products pr;
   };
   Tables tb;
+  alignas(16) _Float16 fb[4][2][16][16];  // flagged blocks: exact diagonal tiles of A (x beta) and P
+  DiagFlags df;
 };
 
 struct Streams {
@@ -209,17 +231,23 @@ __device__ __forceinline__ void produce(Smem& sm, int l, f4* Oacc) {
     }
     const int r = 16 * R + lr, j0 = 16 * J + 4 * lg;
     f4 a = acc[t];
-    if (R == J) {
+    if (R == J && ((__builtin_amdgcn_readfirstlane(sm.df.bits) >> R) & 1)) {
+      // flagged block: the exact tile formed while the chunk was staged (masked, A times beta)
+      const h4 x = *reinterpret_cast<const h4*>(&sm.fb[R][kind][lr][4 * lg]);
+      a = f4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    } else {
+      if (R == J) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = j0 + i;
-        if (kind ? (j > r) : (j >= r)) a[i] = 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int j = j0 + i;
+          if (kind ? (j > r) : (j >= r)) a[i] = 0.f;
+        }
       }
+      if (kind == 0) a *= sm.tb.beta[r];
     }
     if (kind == 1) {
       *reinterpret_cast<h4*>(&sm.pr.p[r][j0]) = to_h4(a);
     } else {
-      a *= sm.tb.beta[r];
       if (R == J)
         invert_diag(sm, J, a, lr, lg);
       else
@@ -246,13 +274,117 @@ __device__ __forceinline__ void o_tile(int w, int t, int& cb, int& db) {
   db = idx & 1;
 }
 
+// Blocks flagged as too strongly gated for the middle-token split (bits of `flags`): after the
+// regular staging, each thread stages its own rows of those blocks again with the state
+// entering the block, G_b = G_{16R-1} (0 for the first block), as the rows' reference, so every
+// factor is <= 1: k_r e^{G_r - G_b}, k_r e^{G_end - G_r}, k_r e^{G_63 - G_r}, q_r e^{G_r - G_b},
+// and the tables e^{G_b}, e^{G_b - G_end(J)}.  The middle-token keys of those blocks are unused
+// (zeroed): their diagonal 16x16 tiles of A and P are formed exactly instead,
+// A_rj = beta_r sum_c k_rc k_jc e^{G_rc - G_jc} (j < r), P_rj = sum_c q_rc k_jc e^{G_rc - G_jc}
+// (j <= r), each factor (<= 1) computed in fp32 from the prefix of its own pair and channel.
+// Rows are read again from the inputs (zeros past the end of the stream).  A call outside the
+// regular path, so the registers of that path are not shaped by it; every thread calls it.
+struct FlagArgs {  // what the slow path reads besides the LDS (passed by value: no copy of the kernel arguments)
+  const void *q, *k, *beta;
+  int64_t T, bh, t0;
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, const FlagArgs& f, int64_t per_tok) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)base + f.bh * f.T * per_tok), 0,
+                                           (int)(f.T * per_tok * 2), kRsrcWord3);
+}
+__device__ __noinline__ void restage_flagged(Smem& sm, FlagArgs f, int flags, int tid) {
+  const int t = tid & 255, g8 = t & 15, rq = t >> 4, R = rq >> 2;
+  const int64_t t0 = f.t0;
+  const auto rows = row_rsrc(tid >= 256 ? f.q : f.k, f, D);
+  if ((flags >> R) & 1) {
+    const float* Ge = &sm.pf.G[16 * R + 15][8 * g8];
+    const float* Gl = &sm.pf.G[C - 1][8 * g8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * rq + i;
+      const v4u x = __builtin_amdgcn_raw_buffer_load_b128(rows, (int)(((t0 + row) * D + 8 * g8) * 2), 0, 0);
+      const float* Gr = &sm.pf.G[row][8 * g8];
+      h8 a, b, c, d;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = bf_at(x, e), gb = R ? sm.pf.G[16 * R - 1][8 * g8 + e] : 0.f;
+        const float er = __expf(fminf(Ge[e] - Gr[e], 0.f));                 // e^{G_end - G_r}
+        a[e] = (_Float16)(v * __expf(fminf(Gr[e] - gb, 0.f)));              // e^{G_r - G_b}
+        b[e] = (_Float16)(v * er);
+        c[e] = (_Float16)(v * er * __expf(fminf(Gl[e] - Ge[e], 0.f)));      // e^{G_63 - G_r}
+        d[e] = (_Float16)0.f;
+      }
+      if (tid < 256) {
+        *reinterpret_cast<h8*>(&sm.kl[row][8 * g8]) = a;
+        *reinterpret_cast<h8*>(&sm.kd[row][8 * g8]) = d;
+        *reinterpret_cast<h8*>(&sm.kr[row][8 * g8]) = b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.kt[8 * g8 + e][kt_col(8 * g8 + e, row)] = c[e];
+      } else {
+        *reinterpret_cast<h8*>(&sm.ql[row][8 * g8]) = a;
+      }
+    }
+  }
+  if (tid >= 384) {  // tables of the flagged blocks, one channel per thread (the regular writers)
+    const int ch = tid - 384;
+    for (int R2 = 0; R2 < 4; ++R2) {
+      if (!((flags >> R2) & 1)) continue;
+      const float gb = R2 ? sm.pf.G[16 * R2 - 1][ch] : 0.f;
+      sm.tb.em[R2][ch] = __expf(gb);
+      for (int J2 = 0; J2 < R2; ++J2) sm.tb.fm[R2][J2][ch] = __expf(fminf(gb - sm.pf.G[16 * J2 + 15][ch], 0.f));
+    }
+  }
+  // exact diagonal tiles: two threads per pair (r, j), 64 channels each
+  const int pr = tid >> 1, r = pr >> 4, j = pr & 15, c0 = 64 * (tid & 1);
+  const auto krs = row_rsrc(f.k, f, D), qrs = row_rsrc(f.q, f, D), brs = row_rsrc(f.beta, f, 1);
+  for (int B = 0; B < 4; ++B) {
+    if (!((flags >> B) & 1)) continue;
+    const int64_t tr = t0 + 16 * B + r, tj = t0 + 16 * B + j;
+    float sa = 0.f, sp = 0.f;
+    if (j <= r) {
+      for (int c = c0; c < c0 + 64; c += 8) {
+        const v4u kr = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)((tr * D + c) * 2), 0, 0);
+        const v4u qr = __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)((tr * D + c) * 2), 0, 0);
+        const v4u kj = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)((tj * D + c) * 2), 0, 0);
+        const float* gr = &sm.pf.G[16 * B + r][c];
+        const float* gj = &sm.pf.G[16 * B + j][c];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float w = bf_at(kj, e) * __expf(fminf(gr[e] - gj[e], 0.f));
+          sa = fmaf(bf_at(kr, e), w, sa);
+          sp = fmaf(bf_at(qr, e), w, sp);
+        }
+      }
+    }
+    sa += __shfl_xor(sa, 1, 64);
+    sp += __shfl_xor(sp, 1, 64);
+    if ((tid & 1) == 0) {
+      const float beta = bf_lo(__builtin_amdgcn_raw_buffer_load_b16(brs, (int)(tr * 2), 0, 0));
+      sm.fb[B][0][r][j] = (_Float16)(r > j ? beta * sa : 0.f);
+      sm.fb[B][1][r][j] = (_Float16)sp;
+    }
+  }
+}
+
 // Stages one chunk (ends with a barrier): the per-channel prefix of log alpha (stage 1, 2a,
 // 2b), then the scaled operand tiles, the per-channel tables, the value slice and beta
 // (stage 3) from the registers of stage_load.  Every thread of the workgroup calls it.
-__device__ __forceinline__ void stage_chunk(Smem& sm, const Stage& st, int tid, int w, int l) {
+__device__ __forceinline__ void stage_chunk(Smem& sm, const Stage& st, const ChunkArgs& p, int64_t bh, int64_t t0,
+                                            int tid, int w, int l) {
   const int t = tid & 255, g8 = t & 15, rq = t >> 4;
-  // ---- stage 1: per-channel prefix of log alpha over each group of 4 tokens
+  // ---- stage 1: per-channel prefix of log alpha over each group of 4 tokens; the largest row
+  // element of each wavefront's block (keys: waves 0..3, queries: waves 4..7, block w % 4)
   float gl[4][8];
+  {
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(bf_at(st.x[i], e)));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (l == 0) sm.df.rowmax[w] = mx;
+  }
   if (tid < 256) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -269,12 +401,24 @@ __device__ __forceinline__ void stage_chunk(Smem& sm, const Stage& st, int tid, 
   }
   __syncthreads();
 
-  // ---- stage 2a: exclusive prefix of the 16 group sums, two channels per lane of wave 4
+  // ---- stage 2a: exclusive prefix of the 16 group sums, two channels per lane of wave 4; the
+  // flags of the blocks too strongly gated for their middle token: G_start - G_m = -(sum of
+  // groups 4R, 4R+1), G_m - G_end = -(sum of groups 4R+2, 4R+3)
   if (w == 4) {
     typedef float f2 __attribute__((ext_vector_type(2)));
     f2 x[16], run = {0.f, 0.f};
 #pragma unroll
     for (int qg = 0; qg < 16; ++qg) x[qg] = *reinterpret_cast<const f2*>(&sm.pf.tot[qg][2 * l]);
+    int bits = 0;
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      const f2 e1 = -(x[4 * R] + x[4 * R + 1]), e2 = -(x[4 * R + 2] + x[4 * R + 3]);
+      const float m = fmaxf(fmaxf(e1[0], e1[1]), fmaxf(e2[0], e2[1]));
+      const float rm = fmaxf(sm.df.rowmax[R], sm.df.rowmax[R + 4]);
+      const float lim = fminf(kDiagExp, __logf(kDiagLimit / rm));  // rm = 0: +inf, no limit
+      if (__ballot(!(m <= lim))) bits |= 1 << R;                 // NaN limit (rm = inf/NaN) flags too
+    }
+    if (l == 0) sm.df.bits = bits;
 #pragma unroll
     for (int qg = 0; qg < 16; ++qg) {
       *reinterpret_cast<f2*>(&sm.pf.tot[qg][2 * l]) = run;
@@ -363,6 +507,9 @@ __device__ __forceinline__ void stage_chunk(Smem& sm, const Stage& st, int tid, 
         sm.tb.gc[ch] = __expf(sm.pf.G[C - 1][ch]);
       }
     }
+    // blocks too strongly gated for their middle token are staged again, by the same threads
+    const int flags = __builtin_amdgcn_readfirstlane(sm.df.bits);
+    if (flags) restage_flagged(sm, FlagArgs{p.q, p.k, p.beta, p.T, bh, t0}, flags, tid);
   }
   __syncthreads();
 }
@@ -434,9 +581,9 @@ using PrepW7 = Jobs<job(1, 3, 3), kNone, kNone, kNone, kNone>;
 // A and P tiles and writing the record.  The inputs of the next record are loaded while the
 // current one is computed (two register sets), and the record writes are never waited for, so
 // neither latency reaches the workgroup's critical path.
-__device__ __forceinline__ void prep_record(Smem& sm, const Stage& st, uint8_t* ws, int64_t rec, int tid, int w,
-                                            int l) {
-  stage_chunk(sm, st, tid, w, l);
+__device__ __forceinline__ void prep_record(Smem& sm, const Stage& st, const ChunkArgs& p, int64_t nchunks, uint8_t* ws,
+                                            int64_t rec, int tid, int w, int l) {
+  stage_chunk(sm, st, p, rec / nchunks, (rec % nchunks) * C, tid, w, l);
   l = opaque(l);
   f4 unused[2];
   switch (w) {
@@ -500,10 +647,10 @@ __global__ __launch_bounds__(NTH, 1) void kda_prep_kernel(ChunkArgs p, uint8_t* 
   load(rec, sa);
   load(rec + step, sb);
   for (; rec < nrec; rec += 2 * step) {  // the bounds are uniform over the workgroup
-    prep_record(sm, sa, ws, rec, tid, w, l);
+    prep_record(sm, sa, p, nchunks, ws, rec, tid, w, l);
     load(rec + 2 * step, sa);
     if (rec + step >= nrec) break;
-    prep_record(sm, sb, ws, rec + step, tid, w, l);
+    prep_record(sm, sb, p, nchunks, ws, rec + step, tid, w, l);
     load(rec + 3 * step, sb);
   }
 }
@@ -549,7 +696,7 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
     const int n = (int)(T - t0 < C ? T - t0 : C);
     __syncthreads();  // the previous chunk is done with every buffer
 
-    stage_chunk(sm, st, tid, w, l);
+    stage_chunk(sm, st, p, bh, t0, tid, w, l);
     if (ci + 1 < nchunks) stage_load(st, sr, t0 + C, tid, c0);
 
     // ---- phase 1: X (waves 0,1), A / P / inverses / O (waves 2..7)

@@ -110,7 +110,8 @@ gdn_status_t gdn_chunk_workspace_size(const gdn_chunk_desc_t* d, int is_kda, siz
  *                             and never stalls the prefill ("Hybrid models...", same section,
  *                             item 1: snapshot capture made asynchronous); the host may read
  *                             them once the stream's work has completed.  Pageable host
- *                             memory is INVALID_VALUE.
+ *                             memory, or a pointer the HIP runtime cannot describe, is
+ *                             INVALID_VALUE.
  *   workspace, workspace_bytes: device workspace, 16-byte aligned, of at least
  *                             gdn_chunk_workspace_size() bytes when one is given.  Only
  *                             the matrix-core KDA prefill uses one (64 KiB per (stream,
@@ -134,7 +135,11 @@ gdn_status_t gdn_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void*
  *   log_alpha [B, H, T, Dk]   in_dtype: one forget rate per key channel
  * ("Attention, Part 4", section 7; "Hybrid Linear Attention Architecture Design
  * Explained", sections 3.1 and 4 -- the division form of the intra-chunk products needs
- * overflow protection, which the kernels provide by per-sub-block reference points).
+ * overflow protection).  The kernels split every decay factor e^{G_r - G_j} at reference
+ * points inside the chunk; a 16-token block whose gates are too strong for its half-precision
+ * split (or whose rows are too large for it) is detected on the device and computed with all
+ * its factors <= 1, its diagonal products in fp32.  Any finite log_alpha <= 0 therefore gives
+ * finite results within the usual tolerance; such blocks only cost extra work.
  */
 gdn_status_t kda_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void* k, const void* v,
                            const void* beta, const void* log_alpha, const float* s0, void* o,

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from gated_deltanet_state_amd import synth
-from helpers import TOL_BF16, rel_l2, say
+from helpers import TOL_BF16, check_streams, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -106,35 +106,39 @@ def test_gdn_mfma_matches_decode_steps():
 
 
 def test_workload_prefill_full_size():
-    """B=4, H=16, T=4096, d=128, chunk 64, bf16; S0 = 0.01 N(0,1): all outputs and final states."""
-    c = synth.WORKLOADS[1]
+    """B=4, H=16, T=4096, d=128, chunk 64, bf16; S0 = 0.01 N(0,1): every output and final state
+    of all 64 streams against the oracle, with bf16 outputs (the workload's) and with fp32
+    outputs (the kernel's own error, without the output rounding).  Whole-tensor and
+    worst-stream relative L2 errors are both bounded."""
     say("prefill workload B=4 H=16 T=4096")
     inp = synth.make_workload(1)
-    o, sf, _ = _gpu(False, inp)
     o_ref, s_ref, _ = _ref(False, inp)
-    eo, es = rel_l2(o, o_ref), rel_l2(sf, s_ref)
-    print(f"prefill workload rel-L2 o={eo:.3e} s_final={es:.3e}")
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    for out_dtype, tol in ((torch.bfloat16, TOL_BF16), (torch.float32, 1e-3)):
+        say(f"prefill workload out={out_dtype}")
+        o, sf, _ = _gpu(False, inp, out_dtype=out_dtype)
+        check_streams(f"prefill o ({out_dtype})", o, o_ref, 2, tol, tol)
+        check_streams(f"prefill s_final ({out_dtype})", sf, s_ref, 2, 1e-3, 1e-3)
+        del o, sf
 
 
-def test_workload_long_prefill_snapshots_sampled_heads():
-    """B=1, H=32, T=65536 with a snapshot every 8192 tokens: the oracle follows 3 sampled
-    heads through the whole sequence (heads are independent); snapshot 8 equals the final
-    state bitwise."""
+def test_workload_long_prefill_snapshots_all_heads():
+    """B=1, H=32, T=65536 with a snapshot every 8192 tokens: all 32 heads through the whole
+    sequence against the oracle (outputs, the 8 snapshots of every head, final states), bf16
+    and fp32 outputs; snapshot 8 equals the final state bitwise."""
     c = synth.WORKLOADS[2]
     say("long prefill workload H=32 T=65536, 8 snapshots")
     inp = synth.make_workload(2)
-    o, sf, sc = _gpu(False, inp, ckpt_every=c.ckpt_every)
-    assert sc.shape == (1, 32, 8, 128, 128)
-    assert torch.equal(sc[:, :, -1], sf)
-    heads = [0, 13, 31]
-    sub = {k: (v[:, heads].contiguous() if v is not None else None) for k, v in inp.items()}
-    o_ref, s_ref, c_ref = _ref(False, sub, ckpt_every=c.ckpt_every)
-    eo = rel_l2(o[:, heads], o_ref)
-    es = rel_l2(sf[:, heads], s_ref)
-    ec = rel_l2(sc[:, heads], c_ref)
-    print(f"long prefill rel-L2 o={eo:.3e} s_final={es:.3e} snapshots={ec:.3e}")
-    assert eo <= TOL_BF16 and es <= TOL_BF16 and ec <= TOL_BF16
+    o_ref, s_ref, c_ref = _ref(False, inp, ckpt_every=c.ckpt_every)
+    for out_dtype, tol in ((torch.bfloat16, TOL_BF16), (torch.float32, 1e-3)):
+        say(f"long prefill out={out_dtype}")
+        o, sf, sc = _gpu(False, inp, ckpt_every=c.ckpt_every, out_dtype=out_dtype)
+        assert sc.shape == (1, 32, 8, 128, 128)
+        assert torch.equal(sc[:, :, -1], sf)
+        check_streams(f"long prefill o ({out_dtype})", o, o_ref, 2, tol, tol)
+        check_streams(f"long prefill s_final ({out_dtype})", sf, s_ref, 2, 1e-3, 1e-3)
+        check_streams(f"long prefill snapshots ({out_dtype})", sc, c_ref, 3, 1e-3, 1e-3)
+        del o, sf, sc
+        torch.cuda.empty_cache()
 
 
 # ------------------------------------------------------------------ KDA (per-channel decay)
@@ -216,18 +220,125 @@ def test_kda_two_kernel_form_is_the_single_kernel(T, every):
         run(ws[:need - 16])
 
 
-def test_workload_kda_full_size_sampled_heads():
-    """B=2, H=32, T=8192, d=128, chunk 64, bf16, per-channel gates: the oracle follows 3
-    sampled (batch, head) streams through the whole sequence."""
-    say("kda workload B=2 H=32 T=8192")
+@pytest.mark.parametrize("form", ["two_kernel", "single_kernel"])
+def test_workload_kda_full_size(form):
+    """B=2, H=32, T=8192, d=128, chunk 64, bf16, per-channel gates: all 64 streams against the
+    oracle, in the two-kernel form (with its workspace, as benchmarked) and the single kernel,
+    bf16 and fp32 outputs; whole-tensor and worst-stream relative L2 errors bounded."""
+    say(f"kda workload B=2 H=32 T=8192 ({form})")
     inp = synth.make_workload(4)
-    o, sf, _ = _gpu(True, inp)
-    sel = [(0, 0), (0, 17), (1, 31)]
-    sub = {k: (torch.stack([v[b, h] for b, h in sel])[None].contiguous() if v is not None else None)
-           for k, v in inp.items()}
-    o_ref, s_ref, _ = _ref(True, sub)
-    og = torch.stack([o[b, h] for b, h in sel])[None]
-    sg = torch.stack([sf[b, h] for b, h in sel])[None]
-    eo, es = rel_l2(og, o_ref), rel_l2(sg, s_ref)
-    print(f"kda workload rel-L2 o={eo:.3e} s_final={es:.3e}")
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    o_ref, s_ref, _ = _kda_workload_ref(inp)
+    ws = None if form == "two_kernel" else False
+    for out_dtype, tol in ((torch.bfloat16, TOL_BF16), (torch.float32, 1e-3)):
+        say(f"kda workload {form} out={out_dtype}")
+        o, sf, _ = _gpu(True, inp, out_dtype=out_dtype, workspace=ws)
+        check_streams(f"kda o ({form}, {out_dtype})", o, o_ref, 2, tol, tol)
+        check_streams(f"kda s_final ({form}, {out_dtype})", sf, s_ref, 2, 1e-3, 1e-3)
+        del o, sf
+
+
+_KDA_REF = {}
+
+
+def _kda_workload_ref(inp):
+    if "r" not in _KDA_REF:
+        _KDA_REF["r"] = _ref(True, inp)
+    return _KDA_REF["r"]
+
+
+@pytest.mark.parametrize("handle", [False, True])
+def test_side_stream_binding_allocations(handle):
+    """Work enqueued on a stream other than torch's current one: the KDA prefill (its workspace
+    and outputs allocated by the binding) and a decode step give the current-stream results bit
+    for bit, while the current stream allocates and overwrites memory of the same size (the
+    binding marks what it allocated as used by the side stream, so none of it is handed out
+    again before the side stream's kernels are done).  The stream is passed as a torch stream
+    or as a raw hipStream_t handle."""
+    import gated_deltanet_state_amd as g
+    say(f"side stream (raw handle={handle})")
+    inp = synth.make_prefill(2, 3, 1000, 128, 128, torch.bfloat16, kda=True, s0_std=0.01, seed=81)
+    d = {k: v.cuda() for k, v in inp.items()}
+    args = [d[k] for k in ("q", "k", "v", "beta", "log_alpha", "s0")]
+    o_ref, s_ref, _ = g.kda_chunk_fwd(*args, out_dtype=torch.float32)
+    dec = synth.make_decode(64, 8, 128, 128, 1, torch.bfloat16, seed=82)
+    st_ref = dec["state"].cuda()
+    dargs = [dec[k][0].cuda() for k in ("q", "k", "v", "beta", "log_alpha")]
+    od_ref = g.gdn_decode_step(st_ref, *dargs)
+    need = g.gdn_chunk_workspace_size(2, 3, 1000, 128, kda=True)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    st = dec["state"].cuda()
+    side.wait_stream(torch.cuda.current_stream())
+    s_arg = side.cuda_stream if handle else side
+    o, sf, _ = g.kda_chunk_fwd(*args, out_dtype=torch.float32, stream=s_arg)
+    od = g.gdn_decode_step(st, *dargs, stream=s_arg)
+    for _ in range(4):   # the current stream churns through blocks of the workspace's size
+        x = torch.empty(need, dtype=torch.uint8, device="cuda")
+        x.fill_(0x5A)
+        y = torch.empty(o.numel() * 4, dtype=torch.uint8, device="cuda")
+        y.fill_(0xA5)
+        del x, y
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(sf, s_ref)
+    assert torch.equal(od, od_ref) and torch.equal(st, st_ref)
+
+
+def _kda_gates(B, H, T, seed, spec):
+    """Per-channel log-gates [B, H, T, 128] for the strong-gate tests (bf16 values)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    la = torch.rand(B, H, T, 128, generator=g) * 0.195 - 0.2          # the usual U[-0.2, -0.005]
+    if spec == "all_strong":                                           # every channel in [-4, -1]
+        la = torch.rand(B, H, T, 128, generator=g) * 3.0 - 4.0
+    elif spec == "few_channels_minus8":                                # 5 channels at -8
+        la[..., [3, 40, 77, 100, 127]] = -8.0
+    elif spec == "strong_chunks":                                      # every other chunk in [-4, -1]
+        for c0 in range(0, T, 128):
+            la[:, :, c0:c0 + 64] = torch.rand(B, H, min(64, T - c0), 128, generator=g) * 3.0 - 4.0
+    elif spec == "extreme":                                            # down to -80 per token
+        la[..., 0::16] = -80.0
+        la[..., 5::16] = -30.0
+        la[:, :, 100:140, 64:] = -12.0
+    return la.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("spec", ["all_strong", "few_channels_minus8", "strong_chunks", "extreme"])
+@pytest.mark.parametrize("form", ["two_kernel", "single_kernel"])
+def test_kda_mfma_any_gate_strength(spec, form):
+    """Per-channel gates far beyond what the middle-token split of a 16-token block can hold in
+    half precision ("Hybrid Linear Attention Architecture Design Explained", section 4: the
+    division form needs overflow protection).  Those blocks are flagged, their rows take the
+    block start as reference and their diagonal tiles are formed exactly, so the results stay
+    finite and match the oracle for any finite log alpha <= 0."""
+    say(f"kda any gate strength: {spec} ({form})")
+    B, H, T = 1, 3, 300
+    inp = synth.make_prefill(B, H, T, 128, 128, torch.bfloat16, kda=True, s0_std=0.01, seed=90)
+    inp["log_alpha"] = _kda_gates(B, H, T, 91, spec)
+    ws = None if form == "two_kernel" else False
+    o_ref, s_ref, _ = _ref(True, inp)
+    for out_dtype, tol in ((torch.float32, 1e-3), (torch.bfloat16, TOL_BF16)):
+        o, sf, _ = _gpu(True, inp, out_dtype=out_dtype, workspace=ws)
+        assert torch.isfinite(o).all() and torch.isfinite(sf).all()
+        eo, es = rel_l2(o, o_ref), rel_l2(sf, s_ref)
+        print(f"kda {spec} {form} out={out_dtype}: rel-L2 o={eo:.3e} s_final={es:.3e}")
+        assert eo <= tol and es <= 1e-3
+
+
+def test_kda_mfma_large_rows_flagged():
+    """Queries of length 1000 (elements up to ~300) with gates that keep the middle-token
+    factors below e^8 (log alpha in [-0.95, -0.85]) but would push rows times factors past
+    half range: the magnitude check flags those blocks too, and the outputs (about 1000 times
+    the usual size) stay finite and match the oracle."""
+    say("kda large rows")
+    B, H, T = 1, 2, 192
+    inp = synth.make_prefill(B, H, T, 128, 128, torch.bfloat16, kda=True, s0_std=0.01, seed=92,
+                             log_alpha_range=(-0.95, -0.85))
+    inp["q"] = (inp["q"].float() * 1000.0).to(torch.bfloat16)
+    o_ref, s_ref, _ = _ref(True, inp)
+    for ws in (None, False):
+        o, sf, _ = _gpu(True, inp, out_dtype=torch.float32, workspace=ws)
+        assert torch.isfinite(o).all() and torch.isfinite(sf).all()
+        eo, es = rel_l2(o, o_ref), rel_l2(sf, s_ref)
+        print(f"kda large rows ws={ws}: rel-L2 o={eo:.3e} s_final={es:.3e}")
+        assert eo <= 1e-3 and es <= 1e-3

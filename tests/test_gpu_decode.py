@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from gated_deltanet_state_amd import synth
-from helpers import rel_l2, say, tol_for
+from helpers import check_streams, rel_l2, say, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -35,28 +35,39 @@ def test_decode_small(D, dtype, out_f32):
     assert rel_l2(st_gpu, st_ref) <= 1e-5
 
 
-def test_decode_workload_full_size_sampled():
-    """256 sequences x 32 heads x 128x128 fp32 states, 100 in-place steps; the oracle follows
-    64 sampled (sequence, head) states through all steps (each state is independent)."""
+def test_decode_workload_full_size():
+    """256 sequences x 32 heads x 128x128 fp32 states, 100 in-place steps: every output of every
+    step and every final state against the oracle.  Errors are bounded over the whole tensor and
+    for the worst (sequence, head) state, over all 100 steps."""
     import gated_deltanet_state_amd as g
     c = synth.WORKLOADS[3]
     say("decode workload: 256x32 states, 100 steps")
     inp = synth.make_workload(3)
-    rng = np.random.default_rng(0)
-    pick = rng.choice(c.N * c.H, 64, replace=False)
-    n_idx, h_idx = pick // c.H, pick % c.H
-    st_ref = inp["state"][n_idx, h_idx].double().numpy()[:, None].copy()   # [64,1,D,D]
-    st = inp["state"].cuda()
     dev_in = {k: inp[k].cuda() for k in ("q", "k", "v", "beta", "log_alpha")}
-    errs = []
-    for t in range(c.steps):
-        o = g.gdn_decode_step(st, *(dev_in[k][t] for k in ("q", "k", "v", "beta", "log_alpha")))
-        sel = [inp[k][t][n_idx, h_idx].unsqueeze(1).contiguous() for k in ("q", "k", "v", "beta", "log_alpha")]
-        o_ref = oracle.decode_step(st_ref, *sel)
-        errs.append(rel_l2(o[n_idx, h_idx].unsqueeze(1), o_ref))
+    runs = {}
+    for out_dt in (torch.bfloat16, torch.float32):   # the workload's outputs, and fp32 outputs
+        st = inp["state"].cuda()
+        outs = [g.gdn_decode_step(st, *(dev_in[k][t] for k in ("q", "k", "v", "beta", "log_alpha")),
+                                  out_dtype=out_dt) for t in range(c.steps)]
+        runs[out_dt] = (st, outs)
     torch.cuda.synchronize()
-    assert max(errs) <= 2e-3, max(errs)
-    assert rel_l2(st[n_idx, h_idx].unsqueeze(1), st_ref) <= 2e-3
+    assert torch.equal(runs[torch.bfloat16][0], runs[torch.float32][0])
+    st_ref = inp["state"].double().numpy().copy()
+    num = {dt: np.zeros((c.N, c.H)) for dt in runs}
+    den = np.zeros((c.N, c.H))
+    for t in range(c.steps):
+        o_ref = oracle.decode_step(st_ref, *(inp[k][t] for k in ("q", "k", "v", "beta", "log_alpha")))
+        den += (o_ref ** 2).sum(-1)
+        for dt, (_, outs) in runs.items():
+            num[dt] += ((outs[t].double().cpu().numpy() - o_ref) ** 2).sum(-1)
+    for dt, tol_stream in ((torch.bfloat16, 2e-3), (torch.float32, 1e-4)):
+        whole, per = (num[dt].sum() / den.sum()) ** 0.5, (num[dt] / den) ** 0.5
+        at = np.unravel_index(np.argmax(per), per.shape)
+        print(f"decode o ({dt}, 100 steps): rel-L2 whole {whole:.3e}, worst state {per.max():.3e} at {at}",
+              flush=True)
+        assert whole <= tol_stream and per.max() <= tol_stream
+    # the states are carried in fp32 arithmetic: far inside the bf16-input bound
+    check_streams("decode final states", runs[torch.float32][0], st_ref, 2, 1e-4, 1e-4)
 
 
 def test_decode_exact_overwrite_on_gpu():

@@ -8,7 +8,7 @@ import torch
 import oracle
 from oracle import serving
 from gated_deltanet_state_amd import synth
-from helpers import rel_l2, say, tol_for
+from helpers import check_streams, rel_l2, say, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -112,11 +112,25 @@ def test_commit_zero_and_no_outputs():
     assert torch.equal(d["pool"], pool0)
 
 
-def test_verify_workload_full_size_sampled():
+def _check_outputs(name, o_bf16, o_f32, o_ref):
+    """Outputs [N, T, H, D] of a window against the oracle, per (sequence, value head).
+
+    With bf16 outputs the whole tensor is held to the bf16 bound; a stream here has only
+    T x 128 values, so its own error is dominated by the output rounding, whose worst case over
+    8,192 streams reaches about 2.2e-3.  The per-stream bound is therefore taken on the fp32
+    outputs of the same kernel, where the arithmetic (fp32 throughout) is the only error."""
+    x, x32 = o_bf16.permute(0, 2, 1, 3), o_f32.permute(0, 2, 1, 3)
+    r = np.transpose(o_ref, (0, 2, 1, 3))
+    check_streams(name + " (bf16)", x, r, 2, 2e-3, 3e-3)
+    check_streams(name + " (fp32)", x32, r, 2, 1e-4, 1e-4)
+
+
+def test_verify_workload_full_size():
     """256 sequences x 32 value heads (16 query/key heads) x 128x128 states in a pool of 512,
     4 draft tokens with the raw gate projections and unnormalised q, k: verification then
-    commit, checked on 12 sampled sequences (sequences are independent) and bit-exact for
-    every pool row no sequence addresses."""
+    commit of the accepted tokens.  Every output of every sequence and every committed pool row
+    against the oracle (whole tensor and worst (sequence, head)); every pool row no sequence
+    addresses is unchanged bit for bit."""
     import gated_deltanet_state_amd as g
     c = synth.SERVING["verify"]
     say("decode_ex verify workload: 256 x 32 heads, T=4, pool 512")
@@ -125,19 +139,37 @@ def test_verify_workload_full_size_sampled():
     kw = dict(slots=d["slots"], qk_l2norm=True, A_log=d["A_log"], dt_bias=d["dt_bias"])
     pool0 = d["pool"].clone()
     o = g.gdn_decode_verify(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], **kw)
+    o32 = g.gdn_decode_verify(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], out_dtype=torch.float32,
+                              **kw)
+    torch.cuda.synchronize()
+    o_ref, _ = _ref(inp, kda=False, raw=True, write_state=False)
+    assert torch.equal(d["pool"], pool0)       # verification writes no state
+    _check_outputs("verify o", o, o32, o_ref)
     g.gdn_decode_commit(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["n_commit"], **kw)
     torch.cuda.synchronize()
-    pick = np.random.default_rng(0).choice(c.N, 12, replace=False)
-    sub = {k: (v[torch.as_tensor(pick)] if k in ("q", "k", "v", "beta", "log_alpha", "slots", "n_commit") else v)
-           for k, v in inp.items()}
-    rows = inp["slots"].numpy()[pick]
-    sub["pool"] = inp["pool"][torch.as_tensor(rows)]
-    sub["slots"] = torch.arange(len(pick), dtype=torch.int32)
-    o_ref, pool_ref = _ref(sub, kda=False, raw=True, write_state=True)
-    assert rel_l2(o[torch.as_tensor(pick)], o_ref) <= 2e-3
-    assert rel_l2(d["pool"][torch.as_tensor(rows)], pool_ref) <= 2e-3
-    unused = np.setdiff1d(np.arange(c.P), inp["slots"].numpy())
+    _, pool_ref = _ref(inp, kda=False, raw=True, write_state=True)
+    rows = inp["slots"].numpy()
+    check_streams("commit pool rows", d["pool"][torch.as_tensor(rows)], pool_ref[rows], 2, 1e-4, 1e-4)
+    unused = np.setdiff1d(np.arange(c.P), rows)
     assert torch.equal(d["pool"][torch.as_tensor(unused)], pool0[torch.as_tensor(unused)])
+
+
+def test_kda_step_workload_full_size():
+    """KDA decode step on 256 sequences x 32 heads of 128x128 states (per-channel gates, one
+    token): every output and every state against the oracle."""
+    import gated_deltanet_state_amd as g
+    c = synth.SERVING["kda"]
+    say("decode_ex kda step workload: 256 x 32 heads, T=1")
+    inp = synth.make_serving(c.N, c.T, c.H, c.Hqk, c.D, c.P, c.dtype, kda=True, s_std=c.s_std, seed=2002)
+    d = _cuda(inp)
+    o32 = g.gdn_decode_ex(d["pool"].clone(), d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], slots=d["slots"],
+                          kda=True, out_dtype=torch.float32)
+    o = g.gdn_decode_ex(d["pool"], d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], slots=d["slots"], kda=True)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = _ref(dict(inp, n_commit=None), kda=True, raw=False, write_state=True, n_commit=False)
+    _check_outputs("kda step o", o, o32, o_ref)
+    rows = inp["slots"].numpy()
+    check_streams("kda step pool rows", d["pool"][torch.as_tensor(rows)], pool_ref[rows], 2, 1e-4, 1e-4)
 
 
 @pytest.mark.parametrize("T", [1, 2, 4, 5, 8, 9])
