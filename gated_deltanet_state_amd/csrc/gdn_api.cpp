@@ -104,10 +104,10 @@ gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, con
     a.dt_bias = pro->raw_gates ? pro->dt_bias : nullptr;
   }
   // Only the matrix-core KDA prefill takes a workspace (its two-kernel form); without one it
-  // runs as a single kernel.  A workspace that is given must be large enough.
+  // runs as a single kernel.  A workspace that holds every record of the call is used in one
+  // slab; a smaller one (at least two records) slab by slab.
   if (workspace && is_kda && gdn::chunk_mfma_supported(a) && a.T > 0) {
-    const size_t need = gdn::kda_workspace_bytes(a);
-    if (workspace_bytes < need || !aligned16(workspace)) return GDN_ERROR_INVALID_VALUE;
+    if (!aligned16(workspace) || workspace_bytes < gdn::kKdaMinWorkspace) return GDN_ERROR_INVALID_VALUE;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
   }

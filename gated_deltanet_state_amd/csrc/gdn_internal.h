@@ -56,8 +56,12 @@ struct DecodeExArgs {
 bool chunk_mfma_supported(const ChunkArgs& a);
 hipError_t launch_chunk_mfma(const ChunkArgs& a, bool kda, hipStream_t stream);
 hipError_t launch_kda_mfma(const ChunkArgs& a, hipStream_t stream);
-// Workspace of the two-kernel matrix-core KDA prefill: one 64 KiB record per (stream, chunk).
+// Workspace of the two-kernel matrix-core KDA prefill: one 64 KiB record per (stream, chunk)
+// for the whole call.  A smaller workspace of at least two records is used slab by slab.
 size_t kda_workspace_bytes(const ChunkArgs& a);
+bool kda_slabs_fit(const ChunkArgs& a, size_t bytes);
+constexpr size_t kKdaMinWorkspace = (size_t)2 << 16;
+
 
 // fp32 vector-unit prefill (fp32 or bf16 inputs, D in {16,32,64,128}, chunk in {16,32,64}).
 bool chunk_valu_supported(const ChunkArgs& a);

@@ -576,14 +576,27 @@ using PrepW5 = Jobs<job(1, 2, 2), job(1, 3, 0), kNone, kNone, kNone>;
 using PrepW6 = Jobs<job(1, 3, 1), job(1, 3, 2), kNone, kNone, kNone>;
 using PrepW7 = Jobs<job(1, 3, 3), kNone, kNone, kNone, kNone>;
 
+static_assert(offsetof(Prefix, tot) >= offsetof(Products, nt), "group sums overlap the record tiles");
+
+// A slab of the two-kernel form: streams bh0 .. bh0 + nbh - 1, chunks c0 .. c0 + nc - 1 of each.
+// Its records sit in the workspace at ((bh - bh0) nc + (ci - c0)) * kRecBytes.  The chain kernel
+// starts each stream from s_in and leaves the state in s_out (both [nbh, D, D] fp32 from stream
+// bh0; s_in null = zeros, s_out null = not kept), so a long sequence runs as consecutive slabs
+// with the state carried between them.
+struct Slab {
+  int64_t bh0, nbh, c0, nc;
+  const float* s_in;
+  float* s_out;
+};
+
 // Records are spread over a grid of at most one workgroup per CU (the LDS holds one); each
 // workgroup walks its records in order, staging each one as the single kernel does, forming the
 // A and P tiles and writing the record.  The inputs of the next record are loaded while the
 // current one is computed (two register sets), and the record writes are never waited for, so
 // neither latency reaches the workgroup's critical path.
-__device__ __forceinline__ void prep_record(Smem& sm, const Stage& st, const ChunkArgs& p, int64_t nchunks, uint8_t* ws,
+__device__ __forceinline__ void prep_record(Smem& sm, const Stage& st, const ChunkArgs& p, const Slab& sl, uint8_t* ws,
                                             int64_t rec, int tid, int w, int l) {
-  stage_chunk(sm, st, p, rec / nchunks, (rec % nchunks) * C, tid, w, l);
+  stage_chunk(sm, st, p, sl.bh0 + rec / sl.nc, (sl.c0 + rec % sl.nc) * C, tid, w, l);
   l = opaque(l);
   f4 unused[2];
   switch (w) {
@@ -598,7 +611,7 @@ __device__ __forceinline__ void prep_record(Smem& sm, const Stage& st, const Chu
   }
   __syncthreads();
   KdaRec* out = reinterpret_cast<KdaRec*>(ws + rec * kRecBytes);
-  for (int e = tid; e < C * D / 8; e += NTH) {  // the X and output operands carry e^{G_m(R)} already
+  for (int e = tid; e < C * D / 8; e += NTH) {  // the X and output operands carry e^{G_ref(R)} already
     const int r = e >> 4, cc = 8 * (e & 15);
     const float* em = &sm.tb.em[r >> 4][cc];
     *reinterpret_cast<h8*>(sat<D>(&out->kl[0][0], r, cc)) = scale8(*reinterpret_cast<const h8*>(&sm.kl[r][cc]), em);
@@ -627,19 +640,19 @@ __device__ __forceinline__ void prep_record(Smem& sm, const Stage& st, const Chu
   if (tid < D) out->gc[tid] = sm.tb.gc[tid];
   if (tid < C) out->beta[tid] = sm.tb.beta[tid];
   // before its first barrier the next record's staging writes only the group sums, which share
-  // no bytes with the tiles read above; everything else it writes comes after that barrier
+  // no bytes with the tiles read above, and the row maxima of its flags; everything else it
+  // writes comes after that barrier
 }
-static_assert(offsetof(Prefix, tot) >= offsetof(Products, nt), "group sums overlap the record tiles");
 
-__global__ __launch_bounds__(NTH, 1) void kda_prep_kernel(ChunkArgs p, uint8_t* ws, int64_t nchunks) {
+__global__ __launch_bounds__(NTH, 1) void kda_prep_kernel(ChunkArgs p, uint8_t* ws, Slab sl) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
-  const int64_t nrec = p.B * p.H * nchunks, step = gridDim.x;
+  const int64_t nrec = sl.nbh * sl.nc, step = gridDim.x;
   auto load = [&](int64_t rec, Stage& st) {
     if (rec >= nrec) return;
-    const int64_t bh = rec / nchunks, ci = rec % nchunks;
+    const int64_t bh = sl.bh0 + rec / sl.nc, ci = sl.c0 + rec % sl.nc;
     stage_load(st, make_streams(p, bh, tid >= 256), ci * C, tid, 0);
   };
   Stage sa, sb;
@@ -647,10 +660,10 @@ __global__ __launch_bounds__(NTH, 1) void kda_prep_kernel(ChunkArgs p, uint8_t* 
   load(rec, sa);
   load(rec + step, sb);
   for (; rec < nrec; rec += 2 * step) {  // the bounds are uniform over the workgroup
-    prep_record(sm, sa, p, nchunks, ws, rec, tid, w, l);
+    prep_record(sm, sa, p, sl, ws, rec, tid, w, l);
     load(rec + 2 * step, sa);
     if (rec + step >= nrec) break;
-    prep_record(sm, sb, p, nchunks, ws, rec + step, tid, w, l);
+    prep_record(sm, sb, p, sl, ws, rec + step, tid, w, l);
     load(rec + 3 * step, sb);
   }
 }
@@ -859,14 +872,14 @@ static_assert(kSplit <= kRecKiB, "copy split");
 // record into nx.
 template <typename TOut>
 __device__ __forceinline__ void chain_chunk(const KdaRec& rc, KdaRec& nx, ChainLocal& loc, int vb, const ChunkArgs& p,
-                                            const Streams& sr, const uint8_t* recs, int64_t ci, int64_t nchunks,
+                                            const Streams& sr, const uint8_t* recs, int64_t ci, int64_t cfirst, int64_t cend,
                                             int64_t bh, int c0, int tid, int w, int l, f4 (&S)[2], v4u& vv) {
   const int64_t T = p.T, t0 = ci * C;
   const int n = (int)(T - t0 < C ? T - t0 : C);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0): this wave's part of the record has landed
   __syncthreads();  // all parts have; chunk ci - 1 is done with the other buffer and value slot
-  const bool more = ci + 1 < nchunks;
-  const uint8_t* next = recs + (ci + 1) * kRecBytes;
+  const bool more = ci + 1 < cend;  // the slab's records run from chunk cfirst to cend - 1
+  const uint8_t* next = recs + (ci + 1 - cfirst) * kRecBytes;
   if (more && tid < 256)
     vv = __builtin_amdgcn_raw_buffer_load_b128(sr.v, (int)((((ci + 1) * C + (tid >> 2)) * D + c0 + 8 * (tid & 3)) * 2), 0, 0);
 
@@ -972,7 +985,7 @@ __device__ __forceinline__ void chain_chunk(const KdaRec& rc, KdaRec& nx, ChainL
 }
 
 template <typename TOut>
-__global__ __launch_bounds__(NTH, 1) void kda_chain_kernel(ChunkArgs p, const uint8_t* ws) {
+__global__ __launch_bounds__(NTH, 1) void kda_chain_kernel(ChunkArgs p, const uint8_t* ws, Slab sl) {
   __shared__ KdaRec rec0;
   __shared__ KdaRec rec1;
   __shared__ ChainLocal loc;
@@ -984,8 +997,8 @@ __global__ __launch_bounds__(NTH, 1) void kda_chain_kernel(ChunkArgs p, const ui
   unsigned bid = blockIdx.x;
   if (nblk % (8 * NT) == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
   const int c0 = (int)(bid % NT) * DVT;
-  const int64_t bh = bid / NT;
-  const int64_t nchunks = (p.T + C - 1) / C;
+  const int64_t rb = bid / NT, bh = sl.bh0 + rb;  // stream of the slab, and of the batch
+  const int64_t cfirst = sl.c0, cend = sl.c0 + sl.nc;
 
   f4 S[2];  // wavefront w: S^T tiles (d_k block w, d_v block db)
   {
@@ -994,32 +1007,33 @@ __global__ __launch_bounds__(NTH, 1) void kda_chain_kernel(ChunkArgs p, const ui
     for (int db = 0; db < 2; ++db) {
       const int dk = 16 * w + 4 * lg, dv = 16 * db + lr;
       f4 x = {0.f, 0.f, 0.f, 0.f};
-      if (p.s0) x = *reinterpret_cast<const f4*>(p.s0 + (bh * D + c0 + dv) * D + dk);
+      if (sl.s_in) x = *reinterpret_cast<const f4*>(sl.s_in + (rb * D + c0 + dv) * D + dk);
       S[db] = x;
       *reinterpret_cast<h4*>(sat<D>(&loc.s[0][0], dv, dk)) = to_h4(x);
     }
   }
 
   const Streams sr = make_streams(p, bh, false);
-  const uint8_t* recs = ws + bh * nchunks * kRecBytes;
+  const uint8_t* recs = ws + rb * sl.nc * kRecBytes;
   v4u vv = {0u, 0u, 0u, 0u};
-  if (nchunks > 0) {
+  if (sl.nc > 0) {
     if (tid < 256)
-      vv = __builtin_amdgcn_raw_buffer_load_b128(sr.v, (int)(((tid >> 2) * D + c0 + 8 * (tid & 3)) * 2), 0, 0);
+      vv = __builtin_amdgcn_raw_buffer_load_b128(sr.v, (int)(((cfirst * C + (tid >> 2)) * D + c0 + 8 * (tid & 3)) * 2), 0, 0);
     fetch_blocks(rec0, recs, w, kRecKiB, NTH / 64, l);
     if (tid < 256) *reinterpret_cast<h8*>(&loc.v[0][tid >> 2][8 * (tid & 3)]) = bf8_to_h8(vv);
   }
-  for (int64_t ci = 0; ci < nchunks; ci += 2) {  // buffers by chunk parity; the bounds are uniform
-    chain_chunk<TOut>(rec0, rec1, loc, 0, p, sr, recs, ci, nchunks, bh, c0, tid, w, l, S, vv);
-    if (ci + 1 < nchunks) chain_chunk<TOut>(rec1, rec0, loc, 1, p, sr, recs, ci + 1, nchunks, bh, c0, tid, w, l, S, vv);
+  for (int64_t ci = cfirst; ci < cend; ci += 2) {  // buffers by chunk parity; the bounds are uniform
+    chain_chunk<TOut>(rec0, rec1, loc, 0, p, sr, recs, ci, cfirst, cend, bh, c0, tid, w, l, S, vv);
+    if (ci + 1 < cend)
+      chain_chunk<TOut>(rec1, rec0, loc, 1, p, sr, recs, ci + 1, cfirst, cend, bh, c0, tid, w, l, S, vv);
   }
 
-  if (p.s_final) {
+  if (sl.s_out) {
     const int lr = l & 15, lg = l >> 4;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int dk = 16 * w + 4 * lg, dv = 16 * db + lr;
-      *reinterpret_cast<f4*>(p.s_final + (bh * D + c0 + dv) * D + dk) = S[db];
+      *reinterpret_cast<f4*>(sl.s_out + (rb * D + c0 + dv) * D + dk) = S[db];
     }
   }
 }
@@ -1031,31 +1045,67 @@ size_t kda_workspace_bytes(const ChunkArgs& a) {
   return (size_t)(a.B * a.H * nchunks) * (size_t)kRecBytes;
 }
 
+// Slab shape for a workspace of `bytes`: every record of the call when they all fit (one slab);
+// otherwise as many streams as leave room for at least one chunk each plus their carried states,
+// and as many chunks as then fit.
+static void kda_slab_shape(int64_t streams, int64_t nchunks, size_t bytes, int64_t& nbh, int64_t& nc) {
+  const int64_t slots = (int64_t)(bytes / (size_t)kRecBytes);
+  if (streams * nchunks <= slots) {
+    nbh = streams;
+    nc = nchunks;
+    return;
+  }
+  nbh = streams * 2 <= slots ? streams : slots / 2;  // each stream: >= 1 record and its state
+  nc = slots / nbh - 1;
+  if (nc > nchunks) nc = nchunks;
+}
+
+bool kda_slabs_fit(const ChunkArgs& a, size_t bytes) { return bytes / (size_t)kRecBytes >= 2 || kda_workspace_bytes(a) <= bytes; }
+
 hipError_t launch_kda_mfma(const ChunkArgs& a, hipStream_t s) {
   const int64_t blocks = a.B * a.H * NT;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const int64_t nchunks = (a.T + C - 1) / C;
-  const size_t need = kda_workspace_bytes(a);
-  const bool two = a.workspace && need > 0 && a.workspace_bytes >= need;
-  if (two) {
-    const int64_t recs = a.B * a.H * nchunks;
-    if (recs > 0x7fffffff) return hipErrorInvalidValue;
-    // one workgroup per CU, each walking every 256th record
-    const int64_t grid = recs < 256 ? recs : 256;
-    hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)grid), dim3(NTH), 0, s, a, static_cast<uint8_t*>(a.workspace),
-                       nchunks);
-    const uint8_t* ws = static_cast<const uint8_t*>(a.workspace);
-    if (a.out_dtype == GDN_BF16)
-      hipLaunchKernelGGL((kda_chain_kernel<__hip_bfloat16>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
-    else
-      hipLaunchKernelGGL((kda_chain_kernel<float>), dim3((unsigned)blocks), dim3(NTH), 0, s, a, ws);
-  } else {
+  const int64_t nchunks = (a.T + C - 1) / C, streams = a.B * a.H;
+  const bool two = a.workspace && nchunks > 0 && kda_slabs_fit(a, a.workspace_bytes);
+  if (!two) {
     if (a.out_dtype == GDN_BF16)
       hipLaunchKernelGGL((kda_chunk_mfma_kernel<__hip_bfloat16>), dim3((unsigned)blocks), dim3(NTH), 0, s, a);
     else
       hipLaunchKernelGGL((kda_chunk_mfma_kernel<float>), dim3((unsigned)blocks), dim3(NTH), 0, s, a);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  // Two-kernel form, slab by slab: for each group of streams, its chunks in order, the state
+  // carried from one slab to the next in the workspace after the slab's records.
+  int64_t nbh, nc;
+  kda_slab_shape(streams, nchunks, a.workspace_bytes, nbh, nc);
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  float* carry = reinterpret_cast<float*>(ws + (size_t)(nbh * nc) * (size_t)kRecBytes);
+  for (int64_t bh0 = 0; bh0 < streams; bh0 += nbh) {
+    const int64_t ns = streams - bh0 < nbh ? streams - bh0 : nbh;
+    for (int64_t c0 = 0; c0 < nchunks; c0 += nc) {
+      Slab sl;
+      sl.bh0 = bh0;
+      sl.nbh = ns;
+      sl.c0 = c0;
+      sl.nc = nchunks - c0 < nc ? nchunks - c0 : nc;
+      const bool first = c0 == 0, last = c0 + sl.nc >= nchunks;
+      sl.s_in = first ? (a.s0 ? a.s0 + bh0 * a.D * a.D : nullptr) : carry;
+      sl.s_out = last ? (a.s_final ? a.s_final + bh0 * a.D * a.D : nullptr) : carry;
+      const int64_t recs = ns * sl.nc;
+      // one workgroup per CU, each walking every 256th record
+      const int64_t grid = recs < 256 ? recs : 256;
+      hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)grid), dim3(NTH), 0, s, a, ws, sl);
+      if (a.out_dtype == GDN_BF16)
+        hipLaunchKernelGGL((kda_chain_kernel<__hip_bfloat16>), dim3((unsigned)(ns * NT)), dim3(NTH), 0, s, a,
+                           (const uint8_t*)ws, sl);
+      else
+        hipLaunchKernelGGL((kda_chain_kernel<float>), dim3((unsigned)(ns * NT)), dim3(NTH), 0, s, a,
+                           (const uint8_t*)ws, sl);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace gdn

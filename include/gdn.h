@@ -73,8 +73,9 @@ typedef struct {
 /*
  * Bytes of device workspace that gdn_chunk_fwd / kda_chunk_fwd can use for `d`
  * (is_kda = 0 or 1): B * H * ceil(T / 64) * 65536 for the matrix-core KDA prefill (its
- * two-kernel form), 0 for every other supported combination.  Errors as for
- * gdn_chunk_fwd's validation.
+ * two-kernel form, every chunk's record at once), 0 for every other supported combination.
+ * A smaller workspace of at least 131072 bytes also works: the two-kernel form then runs in
+ * slabs of streams and chunks that fit it.  Errors as for gdn_chunk_fwd's validation.
  */
 gdn_status_t gdn_chunk_workspace_size(const gdn_chunk_desc_t* d, int is_kda, size_t* bytes);
 
@@ -112,15 +113,17 @@ gdn_status_t gdn_chunk_workspace_size(const gdn_chunk_desc_t* d, int is_kda, siz
  *                             them once the stream's work has completed.  Pageable host
  *                             memory, or a pointer the HIP runtime cannot describe, is
  *                             INVALID_VALUE.
- *   workspace, workspace_bytes: device workspace, 16-byte aligned, of at least
- *                             gdn_chunk_workspace_size() bytes when one is given.  Only
- *                             the matrix-core KDA prefill uses one (64 KiB per (stream,
- *                             chunk)): with it, the state-independent tiles of every chunk
- *                             are formed once, in parallel, by a first kernel, and a second
- *                             kernel runs the sequential part from them (same results, bit
- *                             for bit, as without).  NULL runs the single-kernel form; a
- *                             smaller non-NULL workspace, or one overlapping o, s0, s_final
- *                             or s_ckpt, is INVALID_VALUE.  Everywhere else it is ignored.
+ *   workspace, workspace_bytes: device workspace, 16-byte aligned, when one is given.
+ *                             Only the matrix-core KDA prefill uses one (a 64 KiB record
+ *                             per (stream, chunk)): with it, the state-independent tiles of
+ *                             every chunk are formed once, in parallel, by a first kernel,
+ *                             and a second kernel runs the sequential part from them (same
+ *                             results, bit for bit, as without).  With fewer bytes than
+ *                             gdn_chunk_workspace_size() the two kernels run slab by slab,
+ *                             the state carried between slabs in the workspace.  NULL runs
+ *                             the single-kernel form; a non-NULL workspace under 131072
+ *                             bytes, or one overlapping o, s0, s_final, s_ckpt or the
+ *                             inputs, is INVALID_VALUE.  Everywhere else it is ignored.
  * Supported: Dk == Dv; bf16 inputs with Dk = 128 and chunk = 64 run on the matrix
  * cores; fp32 or bf16 inputs with Dk in {16, 32, 64, 128} and any allowed chunk run on
  * the fp32 vector path.  Other combinations: GDN_ERROR_NOT_SUPPORTED.

@@ -201,7 +201,9 @@ def test_kda_mfma_snapshots_resume_empty():
 def test_kda_two_kernel_form_is_the_single_kernel(T, every):
     """With its workspace the KDA prefill computes every chunk's state-independent tiles in a
     separate parallel kernel; the sequential kernel then runs the same arithmetic on the same
-    operands, so outputs, final state and snapshots equal the single kernel's bit for bit."""
+    operands, so outputs, final state and snapshots equal the single kernel's bit for bit.  The
+    same holds slab by slab, for workspaces that hold only some of the records (streams split
+    into groups, chunks into consecutive slabs with the state carried between them)."""
     import gated_deltanet_state_amd as g
     say(f"kda two-kernel form T={T} every={every}")
     inp = synth.make_prefill(2, 3, T, 128, 128, torch.bfloat16, kda=True, s0_std=0.01, seed=70 + T)
@@ -211,13 +213,17 @@ def test_kda_two_kernel_form_is_the_single_kernel(T, every):
     ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")   # stale bytes must not matter
     run = lambda w: g.kda_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["log_alpha"], d["s0"], ckpt_every=every,
                                     out_dtype=torch.float32, workspace=w)
-    a, b = run(False), run(ws)
-    torch.cuda.synchronize()
-    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
-    if every:
-        assert torch.equal(a[2], b[2])
-    with pytest.raises(g.GdnError):   # a workspace that is too small is refused
-        run(ws[:need - 16])
+    a = run(False)
+    rec = 65536
+    sizes = [need] + [n * rec for n in (2, 3, 7, 13) if n * rec < need]
+    for nb in sizes:
+        b = run(torch.full((nb,), 0xCD, dtype=torch.uint8, device="cuda"))
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), nb
+        if every:
+            assert torch.equal(a[2], b[2]), nb
+    with pytest.raises(g.GdnError):   # a workspace under two records is refused
+        run(ws[:2 * rec - 16])
 
 
 @pytest.mark.parametrize("form", ["two_kernel", "single_kernel"])
