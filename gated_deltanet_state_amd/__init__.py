@@ -21,7 +21,7 @@ __all__ = [
     "GDN_F32", "GDN_BF16", "GDN_SUCCESS", "GDN_ERROR_INVALID_VALUE", "GDN_ERROR_NOT_SUPPORTED",
     "GDN_ERROR_HIP", "GdnChunkDesc", "GdnDecodeExDesc", "gdn_decode_ex", "gdn_decode_verify",
     "gdn_decode_commit", "GdnChunkExDesc", "gdn_chunk_fwd_ex", "gdn_chunk_fwd_ragged", "pack_ragged",
-    "unpack_ragged",
+    "unpack_ragged", "kda_chunk_fwd_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +79,8 @@ def _load() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         f.restype = ci
+    L.kda_chunk_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_chunk_fwd_noalloc.restype = ci
     L.gdn_decode_step.argtypes = [i64, i64, i64, i64, ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
     L.gdn_decode_step.restype = ci
     L.gdn_chunk_fwd_ex.argtypes = [ctypes.POINTER(GdnChunkExDesc)] + [vp] * 13
@@ -267,6 +269,40 @@ def kda_chunk_fwd(q, k, v, beta, log_alpha, s0=None, *, chunk: int = 64, ckpt_ev
     tensor of at least that size is used as given; False runs the single-kernel form."""
     return _chunk_fwd(True, q, k, v, beta, log_alpha, s0, chunk, ckpt_every, out_dtype, o,
                       s_final, s_ckpt, return_final, stream, snapshots_to_host, workspace)
+
+
+def kda_chunk_fwd_noalloc(q, k, v, beta, log_alpha, s0=None, *, o, s_final=None, s_ckpt=None,
+                          ckpt_every: int = 0, chunk: int = 64, stream=None):
+    """kda_chunk_fwd with every output passed in and no allocation anywhere (the library runs on
+    its fixed device scratch, see kda_chunk_fwd_noalloc in include/gdn.h): o [B,H,T,D] is
+    required, s_final [B,H,D,D] fp32 and s_ckpt [B,H,T//ckpt_every,D,D] fp32 when wanted.
+    Calls that overlap on one GPU race on the scratch."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, Dk]")
+    B, H, T, D = q.shape
+    dev, in_dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    L = _Launch(stream)
+    for name, t, shp in (("k", k, (B, H, T, D)), ("v", v, (B, H, T, D)), ("beta", beta, (B, H, T)),
+                         ("log_alpha", log_alpha, (B, H, T, D))):
+        _check(t, name, shp, in_dt, dev)
+    if s0 is not None:
+        _check(s0, "s0", (B, H, D, D), torch.float32, dev)
+    _check(o, "o", (B, H, T, D), o.dtype, dev)
+    if s_final is not None:
+        _check(s_final, "s_final", (B, H, D, D), torch.float32, dev)
+    n_ck = T // ckpt_every if ckpt_every > 0 else 0
+    if n_ck > 0:
+        if s_ckpt is None:
+            raise ValueError("s_ckpt must be passed when ckpt_every > 0 (nothing is allocated here)")
+        _check(s_ckpt, "s_ckpt", (B, H, n_ck, D, D), torch.float32, s_ckpt.device)
+    d = _desc(B, H, T, D, chunk, in_dt, o.dtype, ckpt_every)
+    st = lib.kda_chunk_fwd_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                   _ptr(s0), _ptr(o), _ptr(s_final), _ptr(s_ckpt if n_ck > 0 else None), L.handle)
+    if st != GDN_SUCCESS:
+        raise GdnError(st, "kda_chunk_fwd_noalloc")
+    return o, s_final, s_ckpt
 
 
 def gdn_decode_step(state, q, k, v, beta, log_alpha, *, o=None, out_dtype=None, stream=None):

@@ -77,7 +77,8 @@ struct Prologue {
 gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, const void* k,
                        const void* v, const void* beta, const void* log_alpha, const float* s0,
                        void* o, float* s_final, float* s_ckpt, void* workspace,
-                       size_t workspace_bytes, void* stream, const Prologue* pro = nullptr) {
+                       size_t workspace_bytes, void* stream, const Prologue* pro = nullptr,
+                       bool use_scratch = false) {
   gdn::ChunkArgs a;
   gdn_status_t st = check_chunk_desc(d, is_kda, &a);
   if (st != GDN_SUCCESS) return st;
@@ -179,6 +180,13 @@ gdn_status_t chunk_fwd(int is_kda, const gdn_chunk_desc_t* d, const void* q, con
 
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.log_alpha = log_alpha;
   a.s0 = s0; a.o = o; a.s_final = s_final; a.s_ckpt = s_ckpt;
+  if (use_scratch && is_kda && gdn::chunk_mfma_supported(a) && a.T > 0) {
+    // the allocation-free entry point: the library's fixed device scratch as the workspace
+    if (gdn::kda_scratch(&a.workspace, &a.workspace_bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return GDN_ERROR_HIP;
+    }
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = gdn::chunk_mfma_supported(a) ? gdn::launch_chunk_mfma(a, is_kda != 0, s)
                           : gdn::launch_chunk_valu(a, is_kda != 0, s);
@@ -212,6 +220,12 @@ gdn_status_t kda_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void*
                            void* stream) {
   return chunk_fwd(1, d, q, k, v, beta, log_alpha, s0, o, s_final, s_ckpt, workspace,
                    workspace_bytes, stream);
+}
+
+gdn_status_t kda_chunk_fwd_noalloc(const gdn_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                                   const void* beta, const void* log_alpha, const float* s0, void* o,
+                                   float* s_final, float* s_ckpt, void* stream) {
+  return chunk_fwd(1, d, q, k, v, beta, log_alpha, s0, o, s_final, s_ckpt, nullptr, 0, stream, nullptr, true);
 }
 
 gdn_status_t gdn_chunk_fwd_ex(const gdn_chunk_ex_desc_t* d, const void* q, const void* k, const void* v,

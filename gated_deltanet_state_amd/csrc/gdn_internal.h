@@ -61,7 +61,8 @@ hipError_t launch_kda_mfma(const ChunkArgs& a, hipStream_t stream);
 size_t kda_workspace_bytes(const ChunkArgs& a);
 bool kda_slabs_fit(const ChunkArgs& a, size_t bytes);
 constexpr size_t kKdaMinWorkspace = (size_t)2 << 16;
-
+// Device address and size of the fixed scratch used by the allocation-free KDA entry point.
+hipError_t kda_scratch(void** ptr, size_t* bytes);
 
 // fp32 vector-unit prefill (fp32 or bf16 inputs, D in {16,32,64,128}, chunk in {16,32,64}).
 bool chunk_valu_supported(const ChunkArgs& a);

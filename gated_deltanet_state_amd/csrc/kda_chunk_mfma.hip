@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
+#include <mutex>
+
 #include "gdn_internal.h"
 #include "gdn_mfma_common.h"
 
@@ -1058,6 +1060,35 @@ static void kda_slab_shape(int64_t streams, int64_t nchunks, size_t bytes, int64
   nbh = streams * 2 <= slots ? streams : slots / 2;  // each stream: >= 1 record and its state
   nc = slots / nbh - 1;
   if (nc > nchunks) nc = nchunks;
+}
+
+// Device scratch of the allocation-free entry point (kda_chunk_fwd_noalloc): the two-kernel
+// form's records and carried states, slab by slab.  Each GPU the library runs on holds one copy
+// from the first launch until the process ends.  Calls that overlap on one GPU share it and race.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+
+hipError_t kda_scratch(void** ptr, size_t* bytes) {
+  // The array's name is a host-side stand-in: its device address comes from the runtime, once
+  // per device, with that device current.
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kScratchBytes;
+  return hipSuccess;
 }
 
 bool kda_slabs_fit(const ChunkArgs& a, size_t bytes) { return bytes / (size_t)kRecBytes >= 2 || kda_workspace_bytes(a) <= bytes; }

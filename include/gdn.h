@@ -25,8 +25,8 @@
  *  - Arguments are validated synchronously on the host before anything is launched;
  *    on any error nothing is launched and the status says why.  Work is enqueued
  *    asynchronously on `stream`; the library never synchronises.  A failed launch
- *    returns GDN_ERROR_HIP.  The library holds no mutable global state, so calls from
- *    several host threads are safe.
+ *    returns GDN_ERROR_HIP.  Apart from the scratch of kda_chunk_fwd_noalloc, the library
+ *    holds no mutable global state, so calls from several host threads are safe.
  *  - Device VALUES are not checked.  Preconditions: log_alpha finite and <= 0
  *    (alpha in (0, 1]); beta finite (in (0, 1) on the pages); |q|, |k|, |v| <= 65504
  *    for bf16 inputs (the prefill kernels use half-precision matrix-core operands).
@@ -148,6 +148,23 @@ gdn_status_t kda_chunk_fwd(const gdn_chunk_desc_t* d, const void* q, const void*
                            const void* beta, const void* log_alpha, const float* s0, void* o,
                            float* s_final, float* s_ckpt, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/*
+ * kda_chunk_fwd without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid it).  Same
+ * arguments, results and validation as kda_chunk_fwd minus the workspace: the matrix-core
+ * two-kernel form runs on a fixed 64 MiB scratch array inside the library (one per GPU, held
+ * from the library's first launch on that GPU until the process ends), slab by slab, so any
+ * size is accepted and the scratch never needs more.  The library calls no allocator.
+ * Every call on a GPU shares that GPU's scratch: calls that overlap in time on one GPU (on
+ * different streams, or from several host threads) race and must be serialised by the
+ * caller.  The scratch keeps the last call's contents; every byte a call reads from it is
+ * written by that call first.  GDN_ERROR_HIP if the runtime cannot give the scratch's
+ * device address.
+ */
+gdn_status_t kda_chunk_fwd_noalloc(const gdn_chunk_desc_t* d, const void* q, const void* k, const void* v,
+                                   const void* beta, const void* log_alpha, const float* s0, void* o,
+                                   float* s_final, float* s_ckpt, void* stream);
 
 /*
  * Chunkwise prefill of the gated delta rule with parts of the layer around the core fused

@@ -65,6 +65,20 @@ int main() {
     d = desc();
     if (kda) EXPECT(fwd(kda, &d, 0x6000000, nullptr, P(0x9000000), 16), INV);  // workspace too small
   }
+  // the allocation-free KDA prefill validates like kda_chunk_fwd
+  {
+    gdn_chunk_desc_t d = desc(64, 48);
+    EXPECT(kda_chunk_fwd_noalloc(nullptr, P(0), P(0x1000000), P(0x2000000), P(0x3000000), P(0x4000000), nullptr,
+                                 P(0x6000000), nullptr, nullptr, nullptr), INV);
+    EXPECT(kda_chunk_fwd_noalloc(&d, P(0), P(0x1000000), P(0x2000000), P(0x3000000), P(0x4000000), nullptr,
+                                 P(0x6000000), nullptr, nullptr, nullptr), INV);
+    d = desc();
+    EXPECT(kda_chunk_fwd_noalloc(&d, P(0), P(0x1000000), P(0x2000000), P(0x3000000), P(0x4000000), nullptr,
+                                 P(0x6000008), nullptr, nullptr, nullptr), INV);  // o misaligned
+    d = desc(128, 64, 64);
+    EXPECT(kda_chunk_fwd_noalloc(&d, P(0), P(0x1000000), P(0x2000000), P(0x3000000), P(0x4000000), nullptr,
+                                 P(0x6000000), nullptr, nullptr, nullptr), INV);  // snapshots without a buffer
+  }
   size_t n = 0;
   gdn_chunk_desc_t d = desc(200);
   EXPECT(gdn_chunk_workspace_size(&d, 0, &n), GDN_SUCCESS);

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "gdn_chunk_fwd", "gdn_chunk_fwd_ex", "gdn_chunk_workspace_size", "gdn_decode_ex", "gdn_decode_step",
-        "gdn_status_string", "gdn_version", "kda_chunk_fwd"])
+        "gdn_status_string", "gdn_version", "kda_chunk_fwd", "kda_chunk_fwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(g):
