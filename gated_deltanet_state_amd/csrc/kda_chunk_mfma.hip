@@ -87,7 +87,7 @@ struct alignas(16) Products {
 
 struct alignas(16) Prefix {
   alignas(16) float G[C][LG];           // inclusive prefix of log alpha per channel
-  alignas(16) float tot[16][D];         // sums over groups of 4 tokens
+  alignas(16) float tot[17][D];         // sums over groups of 4 tokens; then their exclusive prefix and the total
 };
 
 struct alignas(16) Smem {
@@ -196,7 +196,7 @@ struct Jobs {
 
 // Gram / score tile (M = j, N = r): the lane holds r = 16 R + lr, j = 16 J + 4 lg + i.
 template <class L>
-__device__ __forceinline__ void produce(Smem& sm, int l, f4* Oacc) {
+__device__ __forceinline__ void produce(Smem& sm, int l, f4* Oacc, int flags) {
   const int lr = l & 15, lg = l >> 4;
   f4 acc[5];
 #pragma unroll
@@ -233,7 +233,7 @@ __device__ __forceinline__ void produce(Smem& sm, int l, f4* Oacc) {
     }
     const int r = 16 * R + lr, j0 = 16 * J + 4 * lg;
     f4 a = acc[t];
-    if (R == J && ((__builtin_amdgcn_readfirstlane(sm.df.bits) >> R) & 1)) {
+    if (R == J && ((flags >> R) & 1)) {
       // flagged block: the exact tile formed while the chunk was staged (masked, A times beta)
       const h4 x = *reinterpret_cast<const h4*>(&sm.fb[R][kind][lr][4 * lg]);
       a = f4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
@@ -371,21 +371,32 @@ __device__ __noinline__ void restage_flagged(Smem& sm, FlagArgs f, int flags, in
 // Stages one chunk (ends with a barrier): the per-channel prefix of log alpha (stage 1, 2a,
 // 2b), then the scaled operand tiles, the per-channel tables, the value slice and beta
 // (stage 3) from the registers of stage_load.  Every thread of the workgroup calls it.
-__device__ __forceinline__ void stage_chunk(Smem& sm, const Stage& st, const ChunkArgs& p, int64_t bh, int64_t t0,
-                                            int tid, int w, int l) {
+__device__ __forceinline__ int stage_chunk(Smem& sm, const Stage& st, const ChunkArgs& p, int64_t bh, int64_t t0,
+                                           int tid, int w, int l) {
   const int t = tid & 255, g8 = t & 15, rq = t >> 4;
   // ---- stage 1: per-channel prefix of log alpha over each group of 4 tokens; the largest row
   // element of each wavefront's block (keys: waves 0..3, queries: waves 4..7, block w % 4)
   float gl[4][8];
   {
-    float mx = 0.f;
+    // bf16 magnitudes order like their bit patterns: an integer max, two per dword, then a DPP
+    // max over the wavefront (lane 63 ends with it)
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    us2 m2 = {0, 0};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(bf_at(st.x[i], e)));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    if (l == 0) sm.df.rowmax[w] = mx;
+      for (int d = 0; d < 4; ++d) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(us2, st.x[i][d] & 0x7fff7fffu));
+    int mx = m2[0] > m2[1] ? m2[0] : m2[1];
+#define GDN_DPP_MAX(ctrl, rows) mx = max(mx, __builtin_amdgcn_update_dpp(mx, mx, ctrl, rows, 0xf, false))
+    GDN_DPP_MAX(0x111, 0xf);  // row_shr:1
+    GDN_DPP_MAX(0x112, 0xf);  // row_shr:2
+    GDN_DPP_MAX(0x114, 0xf);  // row_shr:4
+    GDN_DPP_MAX(0x118, 0xf);  // row_shr:8
+    GDN_DPP_MAX(0x142, 0xa);  // row_bcast:15
+    GDN_DPP_MAX(0x143, 0xc);  // row_bcast:31
+#undef GDN_DPP_MAX
+    const int wmax = __builtin_amdgcn_readlane(mx, 63);
+    if (l == 0) sm.df.rowmax[w] = __uint_as_float((uint32_t)wmax << 16);
   }
   if (tid < 256) {
 #pragma unroll
@@ -403,33 +414,42 @@ __device__ __forceinline__ void stage_chunk(Smem& sm, const Stage& st, const Chu
   }
   __syncthreads();
 
-  // ---- stage 2a: exclusive prefix of the 16 group sums, two channels per lane of wave 4; the
-  // flags of the blocks too strongly gated for their middle token: G_start - G_m = -(sum of
-  // groups 4R, 4R+1), G_m - G_end = -(sum of groups 4R+2, 4R+3)
+  // ---- stage 2a: exclusive prefix of the 16 group sums, two channels per lane of wave 4, and
+  // their total
   if (w == 4) {
     typedef float f2 __attribute__((ext_vector_type(2)));
     f2 x[16], run = {0.f, 0.f};
 #pragma unroll
     for (int qg = 0; qg < 16; ++qg) x[qg] = *reinterpret_cast<const f2*>(&sm.pf.tot[qg][2 * l]);
+#pragma unroll
+    for (int qg = 0; qg < 16; ++qg) {
+      *reinterpret_cast<f2*>(&sm.pf.tot[qg][2 * l]) = run;
+      run += x[qg];
+    }
+    *reinterpret_cast<f2*>(&sm.pf.tot[16][2 * l]) = run;
+  }
+  __syncthreads();
+
+  // ---- stage 2b: add the sums of the earlier groups; publish G.  Wave 5 meanwhile flags the
+  // blocks too strongly gated for their middle token (G_start - G_m = P_{4R} - P_{4R+2},
+  // G_m - G_end = P_{4R+2} - P_{4R+4} for the exclusive group prefix P) or with rows too large
+  // for its factors.
+  if (w == 5) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
     int bits = 0;
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
-      const f2 e1 = -(x[4 * R] + x[4 * R + 1]), e2 = -(x[4 * R + 2] + x[4 * R + 3]);
+      const f2 p0 = *reinterpret_cast<const f2*>(&sm.pf.tot[4 * R][2 * l]);
+      const f2 p2 = *reinterpret_cast<const f2*>(&sm.pf.tot[4 * R + 2][2 * l]);
+      const f2 p4 = *reinterpret_cast<const f2*>(&sm.pf.tot[4 * R + 4][2 * l]);
+      const f2 e1 = p0 - p2, e2 = p2 - p4;
       const float m = fmaxf(fmaxf(e1[0], e1[1]), fmaxf(e2[0], e2[1]));
       const float rm = fmaxf(sm.df.rowmax[R], sm.df.rowmax[R + 4]);
       const float lim = fminf(kDiagExp, __logf(kDiagLimit / rm));  // rm = 0: +inf, no limit
       if (__ballot(!(m <= lim))) bits |= 1 << R;                 // NaN limit (rm = inf/NaN) flags too
     }
     if (l == 0) sm.df.bits = bits;
-#pragma unroll
-    for (int qg = 0; qg < 16; ++qg) {
-      *reinterpret_cast<f2*>(&sm.pf.tot[qg][2 * l]) = run;
-      run += x[qg];
-    }
   }
-  __syncthreads();
-
-  // ---- stage 2b: add the sums of the earlier groups; publish G
   if (tid < 256) {
     const f4 o0 = *reinterpret_cast<const f4*>(&sm.pf.tot[rq][8 * g8]);
     const f4 o1 = *reinterpret_cast<const f4*>(&sm.pf.tot[rq][8 * g8 + 4]);
@@ -447,6 +467,7 @@ __device__ __forceinline__ void stage_chunk(Smem& sm, const Stage& st, const Chu
   __syncthreads();
 
   // ---- stage 3: scaled operand tiles, tables, values, beta
+  const int flags = __builtin_amdgcn_readfirstlane(sm.df.bits);
   {
     const int R = rq >> 2;  // block of this thread's 4 tokens
     const float* Gm = &sm.pf.G[16 * R + 7][8 * g8];
@@ -510,10 +531,10 @@ __device__ __forceinline__ void stage_chunk(Smem& sm, const Stage& st, const Chu
       }
     }
     // blocks too strongly gated for their middle token are staged again, by the same threads
-    const int flags = __builtin_amdgcn_readfirstlane(sm.df.bits);
     if (flags) restage_flagged(sm, FlagArgs{p.q, p.k, p.beta, p.T, bh, t0}, flags, tid);
   }
   __syncthreads();
+  return flags;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -598,18 +619,18 @@ struct Slab {
 // neither latency reaches the workgroup's critical path.
 __device__ __forceinline__ void prep_record(Smem& sm, const Stage& st, const ChunkArgs& p, const Slab& sl, uint8_t* ws,
                                             int64_t rec, int tid, int w, int l) {
-  stage_chunk(sm, st, p, sl.bh0 + rec / sl.nc, (sl.c0 + rec % sl.nc) * C, tid, w, l);
+  const int flags = stage_chunk(sm, st, p, sl.bh0 + rec / sl.nc, (sl.c0 + rec % sl.nc) * C, tid, w, l);
   l = opaque(l);
   f4 unused[2];
   switch (w) {
-    case 0: produce<PrepW0>(sm, l, unused); break;
-    case 1: produce<PrepW1>(sm, l, unused); break;
-    case 2: produce<PrepW2>(sm, l, unused); break;
-    case 3: produce<PrepW3>(sm, l, unused); break;
-    case 4: produce<PrepW4>(sm, l, unused); break;
-    case 5: produce<PrepW5>(sm, l, unused); break;
-    case 6: produce<PrepW6>(sm, l, unused); break;
-    default: produce<PrepW7>(sm, l, unused); break;
+    case 0: produce<PrepW0>(sm, l, unused, flags); break;
+    case 1: produce<PrepW1>(sm, l, unused, flags); break;
+    case 2: produce<PrepW2>(sm, l, unused, flags); break;
+    case 3: produce<PrepW3>(sm, l, unused, flags); break;
+    case 4: produce<PrepW4>(sm, l, unused, flags); break;
+    case 5: produce<PrepW5>(sm, l, unused, flags); break;
+    case 6: produce<PrepW6>(sm, l, unused, flags); break;
+    default: produce<PrepW7>(sm, l, unused, flags); break;
   }
   __syncthreads();
   KdaRec* out = reinterpret_cast<KdaRec*>(ws + rec * kRecBytes);
@@ -711,7 +732,7 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
     const int n = (int)(T - t0 < C ? T - t0 : C);
     __syncthreads();  // the previous chunk is done with every buffer
 
-    stage_chunk(sm, st, p, bh, t0, tid, w, l);
+    const int flags = stage_chunk(sm, st, p, bh, t0, tid, w, l);
     if (ci + 1 < nchunks) stage_load(st, sr, t0 + C, tid, c0);
 
     // ---- phase 1: X (waves 0,1), A / P / inverses / O (waves 2..7)
@@ -745,12 +766,12 @@ __global__ __launch_bounds__(NTH, 1) void kda_chunk_mfma_kernel(ChunkArgs p) {
       }
     } else {
       switch (w) {
-        case 2: produce<JobsW2>(sm, l, Oacc); break;
-        case 3: produce<JobsW3>(sm, l, Oacc); break;
-        case 4: produce<JobsW4>(sm, l, Oacc); break;
-        case 5: produce<JobsW5>(sm, l, Oacc); break;
-        case 6: produce<JobsW6>(sm, l, Oacc); break;
-        default: produce<JobsW7>(sm, l, Oacc); break;
+        case 2: produce<JobsW2>(sm, l, Oacc, flags); break;
+        case 3: produce<JobsW3>(sm, l, Oacc, flags); break;
+        case 4: produce<JobsW4>(sm, l, Oacc, flags); break;
+        case 5: produce<JobsW5>(sm, l, Oacc, flags); break;
+        case 6: produce<JobsW6>(sm, l, Oacc, flags); break;
+        default: produce<JobsW7>(sm, l, Oacc, flags); break;
       }
     }
     __syncthreads();
