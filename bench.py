@@ -475,6 +475,13 @@ def main():
         extra["copy"] = {"bytes_read": 4 * n, "bytes_written": 4 * n, "ms": round(ms, 4),
                          "GBps": round(8 * n / (ms * 1e-3) / 1e9, 1)}
         log(f"copy: {ms:.3f} ms, {8 * n / (ms * 1e-3) / 1e9:.0f} GB/s (read + write)")
+        # a write-only and a read-only kernel of the same size: the two counters in isolation
+        ms_f = time_launches(lambda i: dst.fill_(1.5), 3, 1, torch)
+        acc = torch.empty((), dtype=torch.float32, device=dev)
+        ms_s = time_launches(lambda i: torch.sum(src, out=acc), 3, 1, torch)
+        extra["fill"] = {"bytes_written": 4 * n, "ms": round(ms_f, 4)}
+        extra["sum"] = {"bytes_read": 4 * n, "ms": round(ms_s, 4), "value": float(acc)}
+        log(f"fill: {ms_f:.3f} ms, sum: {ms_s:.3f} ms")
 
     if "metric" not in out:
         print(json.dumps(extra))
