@@ -375,6 +375,143 @@ __global__ __launch_bounds__(kThreads, 4) void decode_ex_kernel(DecodeExArgs a) 
 }
 
 
+// Commit of accepted tokens (the state is written, no outputs) at d = 128, where one state
+// fills the workgroup.  The arithmetic is that of decode_ex_kernel without outputs, token for
+// token, so the two give the same bits; what differs is where the per-token inputs come from.
+// The window's keys (normalised when asked), values and gates, at most kCommitStage tokens,
+// are staged in LDS by one half-wavefront per token, with the loads issued before the
+// state's: the token loop then reads them from LDS and no token waits for a global load of
+// its own.  Longer windows run on decode_ex_kernel.
+constexpr int kCommitStage = 8;
+template <typename TIn, bool KDA>
+__global__ __launch_bounds__(kThreads, 4) void decode_commit128_kernel(DecodeExArgs a) {
+  constexpr int D = 128, LPR = D / 4, RG = 8, RPT = D / RG, W = kCommitStage;
+  static_assert(LPR * RG == kThreads && W * LPR == kThreads, "one state per workgroup, one token per half-wave");
+  __shared__ float ush[D];
+  __shared__ f4v kw[W][LPR];                  // keys, normalised when asked
+  __shared__ float vw[W][D];                  // values
+  __shared__ float bw[W], dw[W];              // beta and the scalar decay
+  __shared__ f4v aw[KDA ? W : 1][LPR];        // per-channel decays (KDA)
+
+  const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
+  const TIn* __restrict__ v = static_cast<const TIn*>(a.v);
+  const TIn* __restrict__ beta = static_cast<const TIn*>(a.beta);
+  const TIn* __restrict__ log_alpha = static_cast<const TIn*>(a.log_alpha);
+
+  const int tid = threadIdx.x;
+  const int64_t s = blockIdx.x;  // (sequence, value head); the whole workgroup drops out together
+  if (s >= a.N * a.H) return;
+  const int64_t n = s / a.H, h = s - n * a.H, hq = h / (a.H / a.Hqk);
+  const int64_t row_slot = a.slots ? static_cast<int64_t>(a.slots[n]) : n;
+  if (row_slot < 0 || row_slot >= a.P) return;
+  int ncommit = a.n_commit ? a.n_commit[n] : static_cast<int>(a.T);
+  ncommit = ncommit < 0 ? 0 : (ncommit > a.T ? static_cast<int>(a.T) : ncommit);
+  if (ncommit == 0) return;
+
+  const int c4 = tid % LPR, rg = tid / LPR;   // as in decode_ex_kernel: rg is the half-wave
+  float A = 0.f, dtb = 0.f;
+  if (!KDA && a.raw_gates) {
+    A = __expf(a.A_log[h]);
+    dtb = a.dt_bias[h];
+  }
+  // staging: half-wave w takes token w, lane c4 its columns 4 c4 .. 4 c4 + 3
+  if (rg < ncommit) {
+    const int w = rg;
+    const int64_t tok = n * a.T + w;
+    const int64_t qk0 = (tok * a.Hqk + hq) * D, g0 = tok * a.H + h;
+    float kk[4], vv[4], al[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kk[j] = ld_in(k, qk0 + 4 * c4 + j);
+      vv[j] = ld_in(v, g0 * D + 4 * c4 + j);
+      if constexpr (KDA) al[j] = ld_in(log_alpha, g0 * D + 4 * c4 + j);
+    }
+    float b = ld_in(beta, g0), g = 0.f;
+    if constexpr (!KDA) g = ld_in(log_alpha, g0);
+    if (a.qk_l2norm) {
+      const float nk = group_sum<LPR>(kk[0] * kk[0] + kk[1] * kk[1] + kk[2] * kk[2] + kk[3] * kk[3]);
+      const float rk = 1.f / sqrtf(nk + 1e-6f);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kk[j] *= rk;
+    }
+    kw[w][c4] = f4v{kk[0], kk[1], kk[2], kk[3]};
+    *reinterpret_cast<f4v*>(&vw[w][4 * c4]) = f4v{vv[0], vv[1], vv[2], vv[3]};
+    if constexpr (KDA) aw[w][c4] = f4v{expf(al[0]), expf(al[1]), expf(al[2]), expf(al[3])};
+    if (c4 == 0) {
+      float dec = 1.f;
+      if constexpr (!KDA) {
+        if (a.raw_gates) {
+          b = 1.f / (1.f + expf(-b));
+          const float x = g + dtb;
+          g = -A * (fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))));  // softplus, no overflow
+        }
+        dec = expf(g);
+      }
+      bw[w] = b;
+      dw[w] = dec;
+    }
+  }
+  StateRows<D, true> S(a.pool + (row_slot * a.H + h) * D * D, rg * LPR + c4);
+  f4v st[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) st[i] = S.load(i * RG * LPR);
+  __syncthreads();
+
+  // The state is kept as cs S' with a running scale cs, the product of the decays so far: a
+  // token adds (u / cs) k^T to S' with one FMA per element.  A token whose decay would take cs
+  // below 2^-60 first multiplies cs and its own decay into the rows (any decay, 0 included)
+  // and continues from cs = 1, so 1 / cs stays finite.
+  float cs = 1.f;
+#pragma unroll 1
+  for (int t = 0; t < ncommit; ++t) {
+    const f4v kv = kw[t][c4];
+    const float kk[4] = {kv[0], kv[1], kv[2], kv[3]};
+    // the gates are the same in every lane: scalar registers, so the branch below is uniform
+    const float b = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bw[t])));
+    const float dec = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(dw[t])));
+    if constexpr (KDA) {
+      const f4v al = aw[t][c4];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) st[i] *= al;
+    }
+    const float cn = cs * dec;
+    float rc;
+    if (cn >= 0x1p-60f) {
+      cs = cn;
+      rc = 1.f / cn;
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) st[i] = (st[i] * cs) * dec;
+      cs = 1.f;
+      rc = 1.f;
+    }
+    float vals[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      vals[i] = st[i][0] * kk[0] + st[i][1] * kk[1] + st[i][2] * kk[2] + st[i][3] * kk[3];
+    reduce_scatter<RPT>(vals, c4);
+    const float r = vals[0] + xor_lane<RPT>(vals[0]);
+    const int row = rg + RG * (c4 & (RPT - 1));
+    // r is S'_{t-1} k and the stored correction is u / cs = beta (v / cs - r)
+    if (c4 < RPT) ush[row] = b * (vw[t][row] * rc - r);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const float ui = ush[rg + RG * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st[i][j] += ui * kk[j];
+    }
+    // the next token overwrites the corrections only after every lane has read them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) S.store(i * RG * LPR, st[i] * cs);
+}
+
 // ------------------------------------------------------------------------------------------
 // Matrix-core form of draft-token verification (outputs only, the state is not written) for
 // the scalar gate at d = 128 and windows of at most 8 tokens.  The window is one chunk of the
@@ -424,6 +561,7 @@ __global__ __launch_bounds__(256, 8) void decode_win_mfma_kernel(DecodeExArgs a)
   } lu;
   __shared__ float gpart[4][16][16];            // per wave: Gram over its quarter of the key channels
   __shared__ float gsh[4][16][16];              // Gram of the window's rows [k_0..k_{W-1}, q_0..q_{W-1}]
+  __shared__ __align__(16) TIn vsh[kWinMax][D]; // the window's values, as stored
   auto& ash = lu.ash;
   auto& rsh = lu.rsh;
 
@@ -465,6 +603,14 @@ __global__ __launch_bounds__(256, 8) void decode_win_mfma_kernel(DecodeExArgs a)
     ld4(src + 4, live, y);
     *reinterpret_cast<f4*>(&ash[r][c]) = f4{x[0], x[1], x[2], x[3]};
     *reinterpret_cast<f4*>(&ash[r][c + 4]) = f4{y[0], y[1], y[2], y[3]};
+    // the value rows, copied as stored (16-byte pieces), by the threads of the key rows
+    if (r < W) {
+      typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+      const u4* vs = reinterpret_cast<const u4*>(v + ((n * a.T + r) * a.H + h) * D + c);
+      u4* vd = reinterpret_cast<u4*>(&vsh[r][c]);
+#pragma unroll
+      for (int e = 0; e < static_cast<int>(8 * sizeof(TIn) / 16); ++e) vd[e] = vs[e];
+    }
   }
 
   // gates of the window: lane t < W loads beta_t and log alpha_t (formed after the products)
@@ -550,7 +696,7 @@ __global__ __launch_bounds__(256, 8) void decode_win_mfma_kernel(DecodeExArgs a)
       if (t >= W) continue;  // uniform
       const int64_t tok = n * a.T + t;
       const float gam = __expf(G[t]);
-      float x = bt[t] * (ld_in(v, (tok * a.H + h) * D + dv) - gam * rk[t] * rsh[w][t][l]);
+      float x = bt[t] * (ld_in(&vsh[t][0], dv) - gam * rk[t] * rsh[w][t][l]);
       float dq[kWinMax];  // e^{G_t - G_j} / |k_j|, j <= t
 #pragma unroll
       for (int j = 0; j <= t; ++j) dq[j] = __expf(G[t] - G[j]) * rk[j];
@@ -576,9 +722,11 @@ hipError_t launch_decode_ex_t(const DecodeExArgs& a, hipStream_t stream) {
     // Verification windows (outputs only) take the matrix-core form.  A window that writes the
     // state stays on the row-coalesced kernel: reading and writing every state is HBM-bound
     // there already, and the accumulator layout moves the state in 64-byte pieces per row.
-    // its key/query loads move 4 elements at once: the bases must be aligned to that
+    // its key/query loads move 4 elements at once and its value copies 16 bytes: the bases
+    // must be aligned to that
     const uintptr_t qk_align = 4 * sizeof(TIn);
-    const bool qk_aligned = (reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k)) % qk_align == 0;
+    const bool qk_aligned = (reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k)) % qk_align == 0 &&
+                            reinterpret_cast<uintptr_t>(a.v) % 16 == 0;
     if (!a.kda && !a.write_state && a.o && a.T <= kWinMax && qk_aligned && units <= 0x7fffffff) {
       hipLaunchKernelGGL((decode_win_mfma_kernel<TIn, TOut>), dim3(static_cast<unsigned>(units)), dim3(256), 0,
                          stream, a);
@@ -586,6 +734,13 @@ hipError_t launch_decode_ex_t(const DecodeExArgs& a, hipStream_t stream) {
     }
   }
   const dim3 grid(static_cast<unsigned>(blocks));
+  if constexpr (D == 128) {
+    if (a.write_state && !a.o && a.T <= kCommitStage) {
+      if (a.kda) hipLaunchKernelGGL((decode_commit128_kernel<TIn, true>), grid, dim3(kThreads), 0, stream, a);
+      else hipLaunchKernelGGL((decode_commit128_kernel<TIn, false>), grid, dim3(kThreads), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (a.kda) {
     if (a.o) hipLaunchKernelGGL((decode_ex_kernel<D, TIn, TOut, true, true>), grid, dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL((decode_ex_kernel<D, TIn, TOut, true, false>), grid, dim3(kThreads), 0, stream, a);

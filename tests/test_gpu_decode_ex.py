@@ -252,8 +252,9 @@ def test_commit_strong_decay_against_oracle(D, T):
     """Commit keeps the state as a running scale times rows and folds the scale in once the
     decays' product would fall below 2^-60.  Gates that cross that point at different tokens
     (log alpha -15 per token folds at the third; -50 folds at once; -30/-2 alternate; -0.01
-    never folds), every token committed, fp32 inputs: pool rows against the oracle.  A window
-    of 33 tokens folds many times along the way."""
+    never folds; one token at -200, whose decay is 0 in fp32), every token committed, fp32
+    inputs: pool rows against the oracle.  A window of 33 tokens folds many times along the
+    way."""
     import gated_deltanet_state_amd as g
     N, H, Hqk, P = 5, 4, 2, 9
     say(f"commit strong decay D={D} T={T}")
@@ -265,6 +266,7 @@ def test_commit_strong_decay_against_oracle(D, T):
     la[2, 0::2], la[2, 1::2] = -30.0, -2.0
     la[3] = -0.01
     la[4] = torch.linspace(-40.0, -1.0, T).view(T, 1)
+    la[3, T // 2] = -200.0
     inp["log_alpha"] = la
     inp["n_commit"] = torch.full((N,), T, dtype=torch.int32)
     d = _cuda(inp)
