@@ -100,6 +100,7 @@ struct alignas(16) Smem {
   alignas(16) _Float16 u[DVT][LK];       // U of the chain's chunk                [d_v][token]
   alignas(16) Gates gt[3];
   alignas(16) float rq[C];               // 1 / |q_r| of the queries' chunk when the kernel normalises them
+  alignas(16) float gin[2][2][C];        // raw gates: beta, log alpha of a chunk, activated, by chunk mod 2
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
 __device__ __forceinline__ int kbuf(int chunk) { return (chunk + 3) % 3; }  // chunk >= -3
@@ -643,6 +644,7 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, cons
   RowStage<1, L2N> qa(p.q, str, l), qb(p.q, str, l);
   Set sa, sb;
   auto load_g = [&](Set& st, int64_t t0) {
+    if constexpr (RAW) return;  // raw gates arrive activated, through sm.gin
     st.bb = __builtin_amdgcn_raw_buffer_load_b16(br, (int)((t0 + l) * 2), 0, 0);
     st.gg = __builtin_amdgcn_raw_buffer_load_b16(gr, (int)((t0 + l) * 2), 0, 0);
   };
@@ -658,23 +660,16 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, cons
   load_v(sa, -C);
   qb.load(0);
   load_v(sb, 0);
-  // raw gate projections (layer prologue): beta = sigmoid(b), log alpha = -exp(A_log) softplus(a + dt_bias)
-  float Aexp = 0.f, dtb = 0.f;
-  if constexpr (RAW) {
-    const int64_t h = str.st % p.H;
-    Aexp = __expf(p.A_log[h]);
-    dtb = p.dt_bias[h];
-  }
   auto iter = [&](int c, Set& st, RowStage<1, L2N>& qs) {
     float dl, bgam;  // e^{G_63 - G_l} and beta gamma of chunk c + 2, scaled by 1 / |k_l| in phase 2 with L2N
     {
-      float g = bf16_bits_to_f32(st.gg & 0xffffu), bt = bf16_bits_to_f32(st.bb & 0xffffu);
-      if constexpr (RAW) {
-        // tokens past the end read as b = a = 0; they must stay identity steps
-        const bool live = (int64_t)(c + 2) * C + l < T;
-        const float xa = g + dtb;
-        g = live ? -Aexp * (fmaxf(xa, 0.f) + log1pf(__expf(-fabsf(xa)))) : 0.f;
-        bt = live ? 1.f / (1.f + __expf(-bt)) : 0.f;
+      float g, bt;
+      if constexpr (RAW) {  // activated by the query wave one iteration ago
+        bt = sm.gin[(c + 2) & 1][0][l];
+        g = sm.gin[(c + 2) & 1][1][l];
+      } else {
+        g = bf16_bits_to_f32(st.gg & 0xffffu);
+        bt = bf16_bits_to_f32(st.bb & 0xffffu);
       }
       const float x = wave_prefix_sum(g);
       const float glast = __shfl(x, C - 1, 64);
@@ -726,12 +721,47 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, cons
 }
 
 // Role: first half of the queries of chunk c + 1 (wave 9, phase 2), loaded two iterations ahead.
-template <bool L2N>
+// With raw gates, phase 1 (otherwise idle) takes the gate activations off the gates wave:
+// beta = sigmoid(b) and log alpha = -exp(A_log) softplus(a + dt_bias) of chunk c + 3 ("Attention,
+// Part 4", section "Where alpha and beta come from"), into sm.gin (by chunk mod 2) for the gates
+// wave's next iteration; b and a are loaded one iteration before.  Tokens past the end read as
+// b = a = 0 and must stay identity steps, so they take beta = log alpha = 0.
+template <bool RAW, bool L2N>
 __device__ __forceinline__ void q_role(Smem& sm, const ChunkArgs& p, const Stream& str, int l, int64_t nchunks) {
   RowStage<0, L2N> qa(p.q, str, l), qb(p.q, str, l);
   qa.load(-C);
   qb.load(0);
+  const int64_t T = str.T;
+  const auto br = stream_rsrc(p.beta, str.tok, T);
+  const auto gr = stream_rsrc(p.log_alpha, str.tok, T);
+  float Aexp = 0.f, dtb = 0.f;
+  uint32_t bb = 0, gg = 0;
+  auto load_g = [&](int chunk) {
+    bb = __builtin_amdgcn_raw_buffer_load_b16(br, (int)(((int64_t)chunk * C + l) * 2), 0, 0);
+    gg = __builtin_amdgcn_raw_buffer_load_b16(gr, (int)(((int64_t)chunk * C + l) * 2), 0, 0);
+  };
+  auto activate = [&](int chunk) {
+    const bool live = (int64_t)chunk * C + l < T;
+    float g = bf16_bits_to_f32(gg & 0xffffu), bt = bf16_bits_to_f32(bb & 0xffffu);
+    const float xa = g + dtb;
+    g = live ? -Aexp * (fmaxf(xa, 0.f) + log1pf(__expf(-fabsf(xa)))) : 0.f;  // softplus, no overflow
+    bt = live ? 1.f / (1.f + __expf(-bt)) : 0.f;
+    sm.gin[chunk & 1][0][l] = bt;
+    sm.gin[chunk & 1][1][l] = g;
+  };
+  if constexpr (RAW) {
+    const int64_t h = str.st % p.H;
+    Aexp = __expf(p.A_log[h]);
+    dtb = p.dt_bias[h];
+    load_g(0);
+    activate(0);  // read by the gates wave in the first iteration
+    load_g(1);
+  }
   auto iter = [&](int c, RowStage<0, L2N>& qs) {
+    if constexpr (RAW) {
+      activate(c + 3);
+      load_g(c + 4);
+    }
     __syncthreads();
     qs.store(sm.q, sm.rq);
     qs.load((int64_t)(c + 3) * C);
@@ -933,7 +963,7 @@ __global__ __launch_bounds__(NTH, 1) void gdn_chunk_mfma_kernel(ChunkArgs p) {
     case 6: key_toff_role<0, L2N>(sm, p, str, l, nchunks); break;
     case 7: key_toff_role<1, L2N>(sm, p, str, l, nchunks); break;
     case 8: gates_qv_role<RAW, L2N>(sm, p, str, c0, l, nchunks); break;
-    case 9: q_role<L2N>(sm, p, str, l, nchunks); break;
+    case 9: q_role<RAW, L2N>(sm, p, str, l, nchunks); break;
     case 10: pa_role<0, L2N>(sm, l, nchunks); break;
     default: pa_role<1, L2N>(sm, l, nchunks); break;
   }

@@ -550,7 +550,8 @@ __device__ __forceinline__ void ld4(const __hip_bfloat16* p, bool live, float (&
   x[2] = __uint_as_float(y.y << 16); x[3] = __uint_as_float(y.y & 0xffff0000u);
 }
 template <typename TIn, typename TOut>
-__global__ __launch_bounds__(256, 8) void decode_win_mfma_kernel(DecodeExArgs a) {
+// (fp32 inputs stage 4 KiB of values instead of 2: their LDS allows 6 workgroups per CU)
+__global__ __launch_bounds__(256, sizeof(TIn) == 2 ? 8 : 6) void decode_win_mfma_kernel(DecodeExArgs a) {
   constexpr int D = 128;
   typedef float f4 __attribute__((ext_vector_type(4)));
   // The staged rows are dead once the products are done; S k_t, S q_t reuse their space (written
