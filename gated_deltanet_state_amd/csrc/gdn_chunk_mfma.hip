@@ -417,6 +417,24 @@ struct RowStage {
       rn[32 * half + 4 * i + rq] = __builtin_amdgcn_rsqf(sum + 1e-6f);  // argument >= 1e-6: no denormal
     }
   }
+  // The row factors alone, from the registers (the same arithmetic as store).
+  __device__ __forceinline__ void norms(float* rn) const {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    float ss[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const h8 y = bf8_to_h8(x[i]);
+      ss[i] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const h2 pr = {y[2 * e], y[2 * e + 1]};
+        ss[i] = __builtin_amdgcn_fdot2(pr, pr, ss[i], false);
+      }
+    }
+    int i;
+    const float sum = row16_reduce_scatter(ss, ch, i);
+    rn[32 * half + 4 * i + rq] = __builtin_amdgcn_rsqf(sum + 1e-6f);
+  }
 };
 
 // Decayed, transposed keys for 4 d_k blocks kb0.. and one 32-token half kc of a chunk: transpose
@@ -608,13 +626,22 @@ __device__ __forceinline__ void key_toff_role(Smem& sm, const ChunkArgs& p, cons
                                               int64_t nchunks) {
   // two register sets: each chunk's rows are loaded two iterations before they are stored
   RowStage<half, L2N> ka(p.k, str, l), kb(p.k, str, l);
+  // wave 7, with q normalisation: the norms of the second half of the queries of chunk c + 1
+  // (phase 2), from rows loaded one iteration before
+  constexpr bool QN = L2N && half == 1;
+  RowStage<1, false> q2(p.q, str, l);
   ka.load(0);
   kb.load(C);
+  if constexpr (QN) q2.load(-C);
   auto iter = [&](int c, RowStage<half, L2N>& ks) {
     ks.store(sm.k[kbuf(c + 2)], sm.gt[kbuf(c + 2)].rk);
     ks.load((int64_t)(c + 4) * C);
     __syncthreads();
     toff_part<half>(sm, c, l);
+    if constexpr (QN) {
+      q2.norms(sm.rq);
+      q2.load((int64_t)(c + 2) * C);
+    }
     __syncthreads();
   };
   __syncthreads();
@@ -641,7 +668,7 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, cons
     uint32_t bb, gg;
     v4u vv[4];
   };
-  RowStage<1, L2N> qa(p.q, str, l), qb(p.q, str, l);
+  RowStage<1, false> qa(p.q, str, l), qb(p.q, str, l);  // their norms come from wave 7
   Set sa, sb;
   auto load_g = [&](Set& st, int64_t t0) {
     if constexpr (RAW) return;  // raw gates arrive activated, through sm.gin
@@ -660,7 +687,7 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, cons
   load_v(sa, -C);
   qb.load(0);
   load_v(sb, 0);
-  auto iter = [&](int c, Set& st, RowStage<1, L2N>& qs) {
+  auto iter = [&](int c, Set& st, RowStage<1, false>& qs) {
     float dl, bgam;  // e^{G_63 - G_l} and beta gamma of chunk c + 2, scaled by 1 / |k_l| in phase 2 with L2N
     {
       float g, bt;
@@ -695,7 +722,7 @@ __device__ __forceinline__ void gates_qv_role(Smem& sm, const ChunkArgs& p, cons
       load_g(st, (int64_t)(c + 4) * C);
     }
     __syncthreads();
-    qs.store(sm.q, sm.rq);
+    qs.store(sm.q, nullptr);
     qs.load((int64_t)(c + 3) * C);
     if constexpr (L2N) {  // the key norms of chunk c + 2 were staged in phase 1
       Gates& gt = sm.gt[kbuf(c + 2)];
