@@ -1,10 +1,12 @@
 // gdn_api.cpp -- the extern "C" entry points of libgdn.so: synchronous host-side
-// validation, then dispatch to one kernel launch on the caller's stream.
+// validation, then dispatch to the kernel launches on the caller's stream (one, except the
+// matrix-core KDA prefill with a workspace: two per slab of the workspace).
 //
-// Nothing here touches device memory or synchronises.  The only HIP call made during
-// validation is the pointer-attribute query on a snapshot buffer (is it device memory or
-// pinned host memory?); every check, that one included, runs before any launch, so a
-// rejected call has launched nothing.
+// Nothing here touches device memory or synchronises.  The HIP calls made during validation
+// are the pointer-attribute query on a snapshot buffer (is it device memory or pinned host
+// memory?) and, for kda_chunk_fwd_noalloc, the device address of its static scratch (taken
+// once per device).  Every check, those included, runs before any launch, so a rejected call
+// has launched nothing.
 #include <stdint.h>
 #include <string.h>
 
