@@ -260,9 +260,10 @@ gdn_status_t gdn_decode_step(int64_t N, int64_t H, int64_t Dk, int64_t Dv, gdn_d
  *             the kernel stops after the committed tokens).  Rows of skipped sequences are
  *             not written.
  * Token t of a sequence sees the state after its tokens 0..t-1 of this window.  A window
- * that only verifies (write_state = 0, o given) with kda = 0, Dk = 128, T <= 8 and q, k
- * aligned to 4 elements is computed as one chunk of the chunkwise form on the fp32 matrix
- * cores; its outputs agree with the token-by-token result to fp32 rounding, not bit for bit.
+ * that only verifies (write_state = 0, o given) with kda = 0, Dk = 128, T <= 8, q, k
+ * aligned to 4 elements and v to 16 bytes is computed as one chunk of the chunkwise form on
+ * the fp32 matrix cores; its outputs agree with the token-by-token result to fp32 rounding,
+ * not bit for bit.  Other windows run token by token.
  * A commit without outputs (write_state = 1, o = NULL, scalar gate) carries the product of
  * the decays as a running scale applied once at the store; the committed rows agree with
  * the token-by-token result to fp32 rounding, not bit for bit.
