@@ -221,8 +221,9 @@ def test_verify_l2norm_plain_gates_one_qk_head(T):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_verify_misaligned_qk_views(dtype):
-    """q and k passed as views one element past an aligned address (allowed by the ABI, which
-    asks only for element alignment) give the same outputs as aligned copies, to rounding."""
+    """q and k, then v, passed as views one element past an aligned address (allowed by the
+    ABI, which asks only for element alignment) give the same outputs as aligned copies, to
+    rounding: such windows take the token loop instead of the matrix-core form."""
     import gated_deltanet_state_amd as g
     N, T, H, D, P = 5, 4, 2, 128, 6
     say(f"decode_ex verify misaligned q/k dtype={dtype}")
@@ -245,6 +246,11 @@ def test_verify_misaligned_qk_views(dtype):
     tol = 1e-5 if dtype == torch.float32 else 2e-3
     assert rel_l2(o_m, o_ref) <= tol and rel_l2(o_a, o_ref) <= tol
     assert rel_l2(o_m, o_a) <= 1e-5
+    vs = shifted(d["v"])
+    assert vs.data_ptr() % 16 != 0
+    o_v = g.gdn_decode_verify(d["pool"], d["q"], d["k"], vs, d["beta"], d["log_alpha"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert rel_l2(o_v, o_ref) <= tol and rel_l2(o_v, o_a) <= 1e-5
 
 
 @pytest.mark.parametrize("D,T", [(16, 6), (128, 6), (128, 33)])
